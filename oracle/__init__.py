@@ -1,0 +1,114 @@
+"""fp64 CPU oracle for the KDA forward pass.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The HIP library never imports or
+links anything here, and nothing here imports the HIP library.
+
+The computation lives in ``kda_oracle.c`` (plain C, fp64, one thread per
+(batch, head) sequence).  It follows eq. (1) of the page
+"Kimi K3：从三条信息流到完整系统", section "KDA 是带逐通道遗忘的 delta rule",
+token by token (decay, then delta correction, then read after write), with
+the bounded gate of eq. (5), section "下界 log-decay 是一个 kernel 设计".
+
+Arrays here use the boundary's layouts: rows ``[B, T, H, D]``, beta
+``[B, T, H]``, states ``[B, H, Dk, Dv]``, all float64.
+
+Parity pins: every function here is pinned by the tests in
+``tests/test_oracle_pins.py`` (worked example, hand-solved scalar case, erase
+identity, beta = 0 and beta -> 0 closed forms, basis-key overwrite, dense
+unrolled products with segment composition, gate bound, split invariance).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB)
+        p, i = ctypes.c_void_p, ctypes.c_int
+        lib.kda_oracle_forward.argtypes = [i, i, i, i, p, p, p, p, i, p, p, p, p, i]
+        lib.kda_oracle_forward.restype = i
+        lib.kda_oracle_gate.argtypes = [p, p, ctypes.c_int64]
+        lib.kda_oracle_gate.restype = None
+        _lib = lib
+    return _lib
+
+
+def default_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def gate(a):
+    """Eq. (5): g = -5 * sigmoid(a), elementwise, fp64."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    g = np.empty_like(a)
+    _load().kda_oracle_gate(_ptr(a), _ptr(g), a.size)
+    return g
+
+
+def forward_units(q, k, v, gate_values, beta, s0=None, gate_is_logit=True, threads=None):
+    """Unit-major entry: q, k, gate [n, T, Dk]; v [n, T, Dv]; beta [n, T];
+    s0 [n, Dk, Dv] or None.  Returns (o [n, T, Dv], S [n, Dk, Dv])."""
+    q, k, v, gv, beta = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, gate_values, beta))
+    n, T, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (n, T, dk) and gv.shape == (n, T, dk) and v.shape == (n, T, dv) and beta.shape == (n, T)
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        assert s0.shape == (n, dk, dv)
+    o = np.empty((n, T, dv), dtype=np.float64)
+    S = np.empty((n, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_forward(n, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(gv), int(bool(gate_is_logit)),
+                                    _ptr(beta), _ptr(s0), _ptr(o), _ptr(S),
+                                    default_threads() if threads is None else int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
+    return o, S
+
+
+def _units(x):
+    """[B, T, H, D] -> [B*H, T, D] (or [B, T, H] -> [B*H, T])."""
+    if x.ndim == 4:
+        B, T, H, D = x.shape
+        return np.ascontiguousarray(x.transpose(0, 2, 1, 3)).reshape(B * H, T, D)
+    B, T, H = x.shape
+    return np.ascontiguousarray(x.transpose(0, 2, 1)).reshape(B * H, T)
+
+
+def forward(q, k, v, beta, a=None, g=None, s0=None, threads=None):
+    """Boundary-layout entry.  q, k, v and a (gate logits) or g (log-decays)
+    are [B, T, H, D]; beta [B, T, H]; s0 [B, H, Dk, Dv] or None.
+    Returns (o [B, T, H, Dv], S_final [B, H, Dk, Dv]) in fp64."""
+    if (a is None) == (g is None):
+        raise ValueError("pass exactly one of a (gate logits) or g (log-decay)")
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    gv = a if a is not None else g
+    s0u = None if s0 is None else np.asarray(s0, dtype=np.float64).reshape(B * H, dk, dv)
+    o, S = forward_units(_units(np.asarray(q, np.float64)), _units(np.asarray(k, np.float64)),
+                         _units(np.asarray(v, np.float64)), _units(np.asarray(gv, np.float64)),
+                         _units(np.asarray(beta, np.float64)), s0u, gate_is_logit=a is not None, threads=threads)
+    o = o.reshape(B, H, T, dv).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(o), S.reshape(B, H, dk, dv)
+
+
+def decode_step(q, k, v, beta, state, a=None, g=None, threads=None):
+    """One recurrent step for every (b, h): q, k, v, a|g [B, H, D]; beta [B, H];
+    state [B, H, Dk, Dv].  Returns (o [B, H, Dv], new state)."""
+    o, S = forward(q[:, None], k[:, None], v[:, None], np.asarray(beta)[:, None],
+                   a=None if a is None else a[:, None], g=None if g is None else g[:, None], s0=state,
+                   threads=threads)
+    return o[:, 0], S

@@ -1,0 +1,114 @@
+"""The oracle pinned to what the pages and the mathematics fix (CPU only).
+
+Each pin in tests/pins.py is run against the oracle; a planted-mistake check
+runs the same pins against deliberately wrong recurrences and gates, so a
+plausible mistake in the oracle (wrong order, sign, index, operand, scale)
+could not pass unnoticed."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import pins
+
+
+def oracle_impl(q, k, v, g, beta, s0):
+    return oracle.forward_units(q, k, v, g, beta, s0, gate_is_logit=False, threads=2)
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle_impl)
+
+
+def test_oracle_gate_bound():
+    pins.pin_gate_bound(oracle.gate)
+
+
+def test_gate_logit_path_matches_log_decay_path():
+    """The logit entry (g = -5 sigmoid(a) inside the oracle) equals the
+    log-decay entry fed with the oracle's own gate values, bit for bit."""
+    rng = np.random.default_rng(11)
+    n, T, d = 2, 9, 8
+    q, k, v, a = (rng.standard_normal((n, T, d)) for _ in range(4))
+    beta = rng.random((n, T))
+    o1, S1 = oracle.forward_units(q, k, v, a, beta, gate_is_logit=True)
+    o2, S2 = oracle.forward_units(q, k, v, oracle.gate(a), beta, gate_is_logit=False)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_boundary_layout_wrapper():
+    """forward() on [B, T, H, D] equals forward_units() per (b, h)."""
+    rng = np.random.default_rng(12)
+    B, T, H, d = 2, 7, 3, 4
+    q, k, v, a = (rng.standard_normal((B, T, H, d)) for _ in range(4))
+    beta = rng.random((B, T, H))
+    s0 = rng.standard_normal((B, H, d, d))
+    o, S = oracle.forward(q, k, v, beta, a=a, s0=s0)
+    for b in range(B):
+        for h in range(H):
+            ou, Su = oracle.forward_units(q[b, :, h][None], k[b, :, h][None], v[b, :, h][None], a[b, :, h][None],
+                                          beta[b, :, h][None], s0[b, h][None])
+            assert np.array_equal(o[b, :, h], ou[0]) and np.array_equal(S[b, h], Su[0])
+
+
+def test_decode_step_is_one_token_of_forward():
+    rng = np.random.default_rng(13)
+    B, H, d, steps = 2, 3, 8, 5
+    q, k, v, a = (rng.standard_normal((B, steps, H, d)) for _ in range(4))
+    beta = rng.random((B, steps, H))
+    s0 = rng.standard_normal((B, H, d, d))
+    o_ref, S_ref = oracle.forward(q, k, v, beta, a=a, s0=s0)
+    S = s0
+    for t in range(steps):
+        o_t, S = oracle.decode_step(q[:, t], k[:, t], v[:, t], beta[:, t], S, a=a[:, t])
+        assert np.array_equal(o_t, o_ref[:, t])
+    assert np.array_equal(S, S_ref)
+
+
+def test_empty_sequence_returns_initial_state():
+    rng = np.random.default_rng(14)
+    s0 = rng.standard_normal((2, 4, 4))
+    e = np.zeros((2, 0, 4))
+    o, S = oracle.forward_units(e, e, e, e, np.zeros((2, 0)), s0)
+    assert o.shape == (2, 0, 4) and np.array_equal(S, s0)
+    o, S = oracle.forward_units(e, e, e, e, np.zeros((2, 0)), None)
+    assert np.array_equal(S, np.zeros((2, 4, 4)))
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(15)
+    n, T, d = 7, 20, 8
+    q, k, v, a = (rng.standard_normal((n, T, d)) for _ in range(4))
+    beta = rng.random((n, T))
+    r1 = oracle.forward_units(q, k, v, a, beta, threads=1)
+    r5 = oracle.forward_units(q, k, v, a, beta, threads=5)
+    assert np.array_equal(r1[0], r5[0]) and np.array_equal(r1[1], r5[1])
+
+
+@pytest.mark.parametrize("name", pins.MUTANTS)
+def test_pins_catch_planted_recurrence_mistake(name):
+    impl = pins.mutant_impl(name)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(impl)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(pins.GATE_MUTANTS))
+def test_pins_catch_planted_gate_mistake(name):
+    with pytest.raises(AssertionError):
+        with np.errstate(over="ignore"):
+            pins.pin_gate_bound(pins.GATE_MUTANTS[name])
+
+
+def test_mutant_harness_is_faithful_without_a_mistake():
+    """The numpy recurrence used for the mutants, run with no mistake,
+    passes every pin (so the mutants fail because of their mistake)."""
+    impl = pins.mutant_impl("none")
+    for pin in pins.ALL_PINS:
+        pin(impl)
