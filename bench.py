@@ -1,0 +1,239 @@
+"""Benchmark of the KDA forward path on one MI355X.
+
+One step = one kda_chunk_fwd call over the prefill workload
+kda_prefill_bf16_b1_h96_t8192 (B=1, T=8192, H=96, d=128, bf16 q/k/v/a, fp32
+beta and state), inputs already resident in HBM.  Printed as one JSON line:
+value = tokens/s; `roofline` is the prefill kernel against HBM (its binding
+roof); `decode` adds kda_decode_step on the decode workload (256 sequences x
+96 heads, fp32 state updated in place, 64 steps with fresh inputs);
+`cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=96,d=128) + decode seq-steps/s; % MFMA/HBM peak"
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+BF16_MFMA_PEAK = 2.5e15    # MI355X dense bf16 MFMA, flop/s
+D = 128
+CHUNK = 16
+# Algorithmic work per token and head (bf16 I/O): read q, k, a, v (2 B each per
+# channel) and beta (4 B), write o (2 B per channel); flops of the chunkwise
+# form at C = 16: 6 d^2 (the three state contractions) + 2 C (3 d + 2 d).
+BYTES_PER_TOKEN_HEAD_BF16 = 2 * (3 * D + D) + 4 + 2 * D   # 1284
+FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * CHUNK * (3 * D + 2 * D)  # 118784
+STATE_BYTES = D * D * 4
+# Decode, per (sequence, head) step: state read + written once, q/k/v/a in, o out.
+DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + BYTES_PER_TOKEN_HEAD_BF16  # 132356
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
+                  for n in ("kda_chunk.hip", "kda_common.h", "kda_decode.hip")]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, launch_bytes):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(kernel)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def timed_launches(fn, n, stream):
+    """Run fn n times back to back; HIP events bracket every launch on the
+    stream the kernel runs on.  Returns per-launch milliseconds."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def bench_prefill(steps, warmup):
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+    from synth.workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS[1]
+    x = device_inputs(w)
+    o = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((w.B, w.H, D, D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"], o=o, final_state=S,
+                          stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    per_launch = timed_launches(step, steps, stream)
+    wall = time.perf_counter() - t0
+    tokens = w.B * w.T
+    launch_bytes = w.B * w.T * w.H * BYTES_PER_TOKEN_HEAD_BF16 + w.B * w.H * STATE_BYTES
+    launch_flops = w.B * w.T * w.H * FLOPS_PER_TOKEN_HEAD
+    avg_ms = sum(per_launch) / len(per_launch)
+    return dict(workload=w, tokens=tokens, wall=wall, per_launch_ms=per_launch, avg_ms=avg_ms,
+                launch_bytes=launch_bytes, launch_flops=launch_flops)
+
+
+def bench_decode(reps=3):
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+    from synth.workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS[4]
+    x = device_inputs(w)
+    steps = [{k: x[k][:, t].contiguous() for k in ("q", "k", "v", "a", "beta")} for t in range(w.T)]
+    for k in ("q", "k", "v", "a", "beta"):
+        del x[k]
+    s0 = x["s0"]
+    state = torch.empty_like(s0)
+    outs = [torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda") for _ in range(w.T)]
+    stream = torch.cuda.current_stream()
+    totals = []
+    per_step = []
+    for rep in range(reps + 1):
+        state.copy_(s0)  # restore the initial state outside the timed region
+        torch.cuda.synchronize()
+        it = iter(range(w.T))
+
+        def one():
+            t = next(it)
+            s = steps[t]
+            kda.kda_decode_step(s["q"], s["k"], s["v"], s["a"], s["beta"], state, o=outs[t], stream=stream)
+
+        ms = timed_launches(one, w.T, stream)
+        if rep > 0:  # the first repetition is the warm-up
+            totals.append(sum(ms))
+            per_step += ms
+    best = min(totals)
+    unit_bytes = w.B * w.H * DECODE_BYTES_PER_UNIT
+    avg_step_ms = sum(per_step) / len(per_step)
+    return dict(workload=w, seq_steps_per_s=w.B * w.T / (best / 1e3), avg_step_ms=avg_step_ms,
+                step_bytes=unit_bytes, steps=w.T, reps=reps)
+
+
+def cpu_baseline(threads):
+    """The oracle as it stands, on a bounded sample of the prefill workload:
+    16 of its 96 heads over all 8192 tokens, on `threads` host threads."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth.workloads import WORKLOADS, host_inputs
+
+    w = WORKLOADS[1]
+    nh = 16
+    h = host_inputs(w, nh=nh, threads=threads)
+    args = (synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]), h["beta"].astype(np.float64))
+    a = synth.to_f64(h["a"])
+    t0 = time.perf_counter()
+    oracle.forward(*args, a=a, threads=threads)
+    dt = time.perf_counter() - t0
+    token_heads = w.B * w.T * nh
+    return {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: heads 0-{nh - 1} of {w.H}, all {w.T} tokens ({token_heads} token-heads, "
+                      f"{dt:.2f} s); value scaled to tokens/s over all {w.H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (every (batch, head) "
+              "sequence is independent; the multi-GPU split is described in DESIGN.md, not run)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import __graft_entry__
+
+    __graft_entry__._ensure_built()
+
+    pre = bench_prefill(args.steps, args.warmup)
+    w = pre["workload"]
+    avg_s = pre["avg_ms"] / 1e3
+    wall_per_step = pre["wall"] / args.steps
+    achieved = pre["launch_bytes"] / avg_s
+    traffic = measured_traffic("chunk_fwd_kernel", pre["launch_bytes"])
+    result = {
+        "metric": METRIC,
+        "value": pre["tokens"] / wall_per_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": D, "d_v": D, "chunk": CHUNK,
+                   "io": "bf16 q/k/v/a/o, fp32 beta and state", "seed": w.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel", "launch_ms": pre["avg_ms"],
+                     "algorithmic_bytes_per_launch": pre["launch_bytes"]},
+        "mfma": {"algorithmic_flops_per_launch": pre["launch_flops"],
+                 "achieved_tflops": pre["launch_flops"] / avg_s / 1e12,
+                 "frac_of_bf16_peak": pre["launch_flops"] / avg_s / BF16_MFMA_PEAK},
+    }
+    if not args.no_decode:
+        torch.cuda.empty_cache()
+        dec = bench_decode()
+        dach = dec["step_bytes"] / (dec["avg_step_ms"] / 1e3)
+        result["decode"] = {
+            "workload": dec["workload"].name, "value": dec["seq_steps_per_s"], "unit": "seq-steps/s",
+            "steps": dec["steps"], "reps": dec["reps"], "ms_per_step": dec["avg_step_ms"],
+            "roofline": {"bound": "hbm", "achieved": dach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK, "traffic": measured_traffic("decode_kernel", dec["step_bytes"]),
+                         "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec["step_bytes"]},
+        }
+    if not args.no_cpu:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        result["cpu_baseline"] = cpu_baseline(threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+"""Python binding of libkda (include/kda.h): the KDA forward pass on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI; torch provides device memory and the stream.  There
+is no fallback: if libkda.so is missing or was not built, every call raises.
+
+    kda_chunk_fwd(q, k, v, a, beta, initial_state=None, o=None, final_state=None)
+        -> (o, final_state)
+    kda_decode_step(q, k, v, a, beta, state, o=None) -> o      (state updated in place)
+
+Layouts (contiguous CUDA tensors): q, k, v, a, o ``[B, T, H, 128]`` (prefill)
+or ``[B, H, 128]`` (decode) in bfloat16 or float32; beta ``[B, T, H]`` /
+``[B, H]`` float32; states ``[B, H, 128, 128]`` float32.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_F32, KDA_BF16 = 0, 1
+D = 128
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded libkda (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build(); there is no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i = ctypes.c_void_p, ctypes.c_int
+        L.kda_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd.restype = i
+        L.kda_decode_step.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
+        L.kda_decode_step.restype = i
+        L.kda_status_string.argtypes = [i]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_version.argtypes = []
+        L.kda_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != KDA_OK:
+        L = lib()
+        raise KdaError(status, f"{L.kda_status_string(status).decode()}: {L.kda_last_error().decode()}")
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v/a must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kda_chunk_fwd(q, k, v, a, beta, initial_state=None, o=None, final_state=None, stream=None):
+    """Chunkwise prefill (kda_chunk_fwd of include/kda.h).  Allocates o and
+    final_state with torch when they are not given.  Returns (o, final_state)."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
+    B, T, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _require(q, "q", (B, T, H, Dk), dt, dev)
+    _require(k, "k", (B, T, H, Dk), dt, dev)
+    _require(a, "a", (B, T, H, Dk), dt, dev)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, T, H, Dv]")
+    Dv = v.shape[3]
+    _require(v, "v", (B, T, H, Dv), dt, dev)
+    _require(beta, "beta", (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (B, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    _require(o, "o", (B, T, H, Dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    _check(lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(initial_state), _ptr(o),
+                               _ptr(final_state), B, T, H, Dk, Dv, code, _stream(dev, stream)))
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, a, beta, state, o=None, stream=None):
+    """One recurrent step (kda_decode_step of include/kda.h); state is
+    updated in place.  Returns o."""
+    import torch
+
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, 128]")
+    B, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _require(k, "k", (B, H, Dk), dt, dev)
+    _require(a, "a", (B, H, Dk), dt, dev)
+    if v.dim() != 3:
+        raise ValueError("v must be [B, H, Dv]")
+    Dv = v.shape[2]
+    _require(v, "v", (B, H, Dv), dt, dev)
+    _require(beta, "beta", (B, H), torch.float32, dev)
+    _require(state, "state", (B, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=dt, device=dev)
+    _require(o, "o", (B, H, Dv), dt, dev)
+    _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(state), _ptr(o), B, H, Dk, Dv,
+                                 code, _stream(dev, stream)))
+    return o
+
+
+def raw_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, stream=0):
+    """Direct call of the C entry point with raw integer pointers; returns
+    the status code without raising (used by the error-path tests)."""
+    return lib().kda_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, stream)
+
+
+def raw_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream=0):
+    return lib().kda_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream)
+
+
+def last_error():
+    return lib().kda_last_error().decode()

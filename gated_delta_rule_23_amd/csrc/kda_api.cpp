@@ -1,0 +1,117 @@
+/*
+ * kda_api.cpp -- the C ABI declared in include/kda.h: argument checks,
+ * dispatch to the gfx950 kernels, and per-thread error text.
+ */
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kda_status ok() { return KDA_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+/* Shared checks of dtype, head sizes and batch/head counts. */
+kda_status check_common(const char* fn, int B, int H, int Dk, int Dv, kda_dtype dtype) {
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+  if (B < 0 || H < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (B=%d, H=%d)", fn, B, H);
+  if (Dk <= 0 || Dv <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: head sizes must be positive (Dk=%d, Dv=%d)", fn, Dk, Dv);
+  if (Dk != 128 || Dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: only Dk = Dv = 128 is implemented (got Dk=%d, Dv=%d)", fn, Dk, Dv);
+  if ((int64_t)B * H > 0x7FFFFFFFll) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H=%lld exceeds the grid limit", fn, (long long)B * H);
+  return KDA_OK;
+}
+
+kda_status check_ptr(const char* fn, const char* name, const void* p) {
+  if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, name);
+  if (!aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, name);
+  return KDA_OK;
+}
+
+#define KDA_TRY(expr)              \
+  do {                             \
+    kda_status _s = (expr);        \
+    if (_s != KDA_OK) return _s;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                         int Dv, kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_chunk_fwd";
+  KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
+  const int64_t units = (int64_t)B * H;
+  if (units == 0) return ok();
+  // every element index (b, t, h, channel) must fit in 63 bits: B*T*H*128 < 2^62
+  if ((double)B * (double)T * (double)H * 128.0 > 4.0e18)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*T*H*128 overflows the index range", fn);
+  KDA_TRY(check_ptr(fn, "final_state", final_state));
+  if (initial_state) KDA_TRY(check_ptr(fn, "initial_state", initial_state));
+  if (T > 0) {
+    KDA_TRY(check_ptr(fn, "q", q));
+    KDA_TRY(check_ptr(fn, "k", k));
+    KDA_TRY(check_ptr(fn, "v", v));
+    KDA_TRY(check_ptr(fn, "a", a));
+    KDA_TRY(check_ptr(fn, "beta", beta));
+    KDA_TRY(check_ptr(fn, "o", o));
+  }
+  hipError_t e = kda::launch_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, dtype == KDA_BF16,
+                                       static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                           float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_decode_step";
+  KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  const int64_t units = (int64_t)B * H;
+  if (units == 0) return ok();
+  KDA_TRY(check_ptr(fn, "q", q));
+  KDA_TRY(check_ptr(fn, "k", k));
+  KDA_TRY(check_ptr(fn, "v", v));
+  KDA_TRY(check_ptr(fn, "a", a));
+  KDA_TRY(check_ptr(fn, "beta", beta));
+  KDA_TRY(check_ptr(fn, "state", state));
+  KDA_TRY(check_ptr(fn, "o", o));
+  hipError_t e = kda::launch_decode(q, k, v, a, beta, state, o, (int)units, dtype == KDA_BF16,
+                                    static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+const char* kda_status_string(kda_status status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+/*
+ * kda_decode.hip -- one recurrent KDA step per (batch, head), state updated
+ * in place (page "Kimi K3：从三条信息流到完整系统", eq. (1) in its expanded
+ * form, section "KDA 是带逐通道遗忘的 delta rule"):
+ *
+ *   alpha = exp(-5 sigmoid(a))
+ *   x = S^T (alpha * k),  y = S^T (alpha * q)        one pass over S
+ *   e = v - x                                          residual vs the decayed prediction
+ *   o = y + beta (q . k) e                             = S_new^T q
+ *   S_new = Diag(alpha) S + beta k e^T                 written back over S
+ *
+ * The step is bound by HBM traffic: each state entry is read once and
+ * written once (2 x 64 KiB per head), against 4 x 128 input values.  One
+ * 256-thread workgroup owns one (b, h) state and keeps it in registers
+ * between the read and the write: thread t holds the float4 columns
+ * 4 (t % 32) .. +3 of rows t / 32 + 8 m, m = 0..15, so every wave reads and
+ * writes two whole 512-byte rows per instruction.
+ */
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
+                                                     const IO* __restrict__ v, const IO* __restrict__ a,
+                                                     const float* __restrict__ beta, float* __restrict__ state,
+                                                     IO* __restrict__ o) {
+  __shared__ float s_alpha[kD], s_ak[kD], s_aq[kD], s_k[kD], s_be[kD];
+  __shared__ f32x4 s_part[8][2][32];  // per row group: partial x and y, float4 per column group
+  __shared__ float s_dot[2];
+
+  const int unit = blockIdx.x;  // b * H + h
+  const int t = threadIdx.x;
+  const size_t row = (size_t)unit * kD;
+  float* S = state + (size_t)unit * kD * kD;
+
+  if (t < kD) {
+    float qi = to_f32(q[row + t]), ki = to_f32(k[row + t]), ai = to_f32(a[row + t]);
+    float al = expf(kGateFloor / (1.0f + expf(-ai)));
+    s_alpha[t] = al;
+    s_ak[t] = al * ki;
+    s_aq[t] = al * qi;
+    s_k[t] = ki;
+    float d = wave_sum(qi * ki);
+    if ((t & 63) == 0) s_dot[t >> 6] = d;
+  }
+
+  const int cg = t & 31, rg = t >> 5;
+  f32x4 s[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg + 8 * m) * kD + 4 * cg);
+  __syncthreads();
+
+  f32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    int i = rg + 8 * m;
+    x += s_ak[i] * s[m];
+    y += s_aq[i] * s[m];
+  }
+  s_part[rg][0][cg] = x;
+  s_part[rg][1][cg] = y;
+  __syncthreads();
+
+  if (t < kD) {
+    const float* px = reinterpret_cast<const float*>(&s_part[0][0][0]);
+    float xs = 0.0f, ys = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      xs += px[(r * 2 + 0) * kD + t];
+      ys += px[(r * 2 + 1) * kD + t];
+    }
+    float bt = beta[unit];
+    float e = to_f32(v[row + t]) - xs;
+    o[row + t] = from_f32<IO>(ys + bt * (s_dot[0] + s_dot[1]) * e);
+    s_be[t] = bt * e;
+  }
+  __syncthreads();
+
+  f32x4 be = *reinterpret_cast<const f32x4*>(&s_be[4 * cg]);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    int i = rg + 8 * m;
+    *reinterpret_cast<f32x4*>(S + (size_t)i * kD + 4 * cg) = s_alpha[i] * s[m] + s_k[i] * be;
+  }
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
+                         void* o, int units, bool bf16_io, hipStream_t stream) {
+  if (units == 0) return hipSuccess;
+  if (bf16_io) {
+    hipLaunchKernelGGL(decode_kernel<bf16>, dim3(units), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o);
+  } else {
+    hipLaunchKernelGGL(decode_kernel<float>, dim3(units), dim3(256), 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, (const float*)a, beta, state, (float*)o);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

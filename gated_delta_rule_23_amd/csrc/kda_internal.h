@@ -1,0 +1,21 @@
+/*
+ * kda_internal.h -- launchers behind the C ABI (include/kda.h).  Arguments
+ * are validated by the caller (kda_api.cpp) before these run.
+ */
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+/* units = B * H workgroups; q, k, v, a, o are [units, 128]; beta [units];
+ * state [units, 128, 128]. */
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
+                         void* o, int units, bool bf16_io, hipStream_t stream);
+
+/* Chunkwise prefill over [B, T, H, 128] rows. */
+hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                            const float* initial_state, void* o, float* final_state, int B, int T, int H,
+                            bool bf16_io, hipStream_t stream);
+
+}  // namespace kda

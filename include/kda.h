@@ -1,0 +1,105 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Kimi K3：从三条信息流到完整系统", wineandchord.com):
+ *   per (batch b, head h), for t = 1..T, with key channels i and value channels j,
+ *     g_t     = -5 * sigmoid(a_t)                       eq. (5), section "下界 log-decay 是一个 kernel 设计"
+ *     alpha_t = exp(g_t)                                 (per key channel, in (e^-5, 1])
+ *     S_t     = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t     = S_t^T q_t                                eq. (1), section "KDA 是带逐通道遗忘的 delta rule"
+ *   The output reads the state after token t's own write, and the decay acts
+ *   before the delta correction, as the reference step in that section fixes.
+ *   S has Dk rows (key channels) and Dv columns (value channels).
+ *   The learned scale e^A of eq. (5) is folded into a by the caller.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a device pointer (hipMalloc'd or equivalent), row-major,
+ *     contiguous and 16-byte aligned.  The library allocates nothing, keeps no
+ *     pointer after returning and holds no global state: it is re-entrant and
+ *     thread-safe.
+ *   - Work is enqueued on `hip_stream` (NULL = the default stream) and runs
+ *     asynchronously; the caller keeps every buffer alive until the stream has
+ *     completed.  No entry point synchronises the host.
+ *   - Arguments are checked before anything is launched.  A non-OK status
+ *     means nothing was enqueued (KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED)
+ *     or the launch itself failed (KDA_ERR_HIP); kda_last_error() then holds a
+ *     description for the calling thread.  Faults during execution surface at
+ *     the caller's next synchronisation.  NaN and out-of-range values are not
+ *     checked; beta is expected in [0, 1].
+ *   - Only Dk = Dv = 128 is implemented (K3's head dimension); other positive
+ *     sizes return KDA_ERR_UNSUPPORTED.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1, /* NULL or misaligned pointer, negative size, overflow, bad enum */
+  KDA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement (Dk, Dv != 128) */
+  KDA_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
+} kda_status;
+
+typedef enum {
+  KDA_F32 = 0,  /* q, k, v, a, o are fp32 */
+  KDA_BF16 = 1  /* q, k, v, a, o are bf16; beta and states stay fp32 */
+} kda_dtype;
+
+/*
+ * Chunkwise prefill: T tokens of B independent sequences, H heads each.
+ * Computed in chunks of 16 tokens (the pages' 16-token tile, whose cumulative
+ * log-decay stays in [-80, 0]: section "下界 log-decay 是一个 kernel 设计"),
+ * inside each chunk by eq. (3)-(4) of section "从投影到 Chunkwise 的完整接口"
+ * and carrying an fp32 state between chunks.
+ *
+ *   q, k, a        [B, T, H, Dk]  dtype                      (read)
+ *   v              [B, T, H, Dv]  dtype                      (read)
+ *   beta           [B, T, H]      fp32                       (read)
+ *   initial_state  [B, H, Dk, Dv] fp32, or NULL for zeros    (read)
+ *   o              [B, T, H, Dv]  dtype                      (written)
+ *   final_state    [B, H, Dk, Dv] fp32                       (written; may be the
+ *                  same buffer as initial_state, any other overlap is undefined)
+ *
+ * T need not be a multiple of 16: the last chunk is partial, with the same
+ * result as padding it with tokens of beta = 0, g = 0 and q = 0.  T = 0 copies
+ * initial_state (or zeros) into final_state; q, k, v, a, beta and o may then
+ * be NULL.  Feeding final_state back as initial_state for the next T' tokens
+ * gives the result of one call over T + T' tokens (up to rounding).
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                         int Dv, kda_dtype dtype, void* hip_stream);
+
+/*
+ * One recurrent decode step: eq. (1) applied to a single token of each of B
+ * sequences and H heads, updating the state in place (read once, written
+ * once).
+ *
+ *   q, k, a   [B, H, Dk]      dtype   (read)
+ *   v         [B, H, Dv]      dtype   (read)
+ *   beta      [B, H]          fp32    (read)
+ *   state     [B, H, Dk, Dv]  fp32    (read, then overwritten with S_t)
+ *   o         [B, H, Dv]      dtype   (written)
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                           float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype,
+                           void* hip_stream);
+
+/* Static text for a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

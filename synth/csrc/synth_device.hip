@@ -57,9 +57,10 @@ extern "C" {
  * arguments, -2 if the launch failed. */
 int synth_rows_device(const synth_row_recipe* recipe, int dtype, int b0, int nb, int t0, int nt, int h0, int nh,
                       void* dst, void* stream) {
-  if (!recipe || !dst || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
+  if (!recipe || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
   uint64_t n = (uint64_t)nb * (uint64_t)nt * (uint64_t)nh;
   if (n == 0) return 0;
+  if (!dst) return -1;
   dim3 grid;
   if (synth_grid(n, &grid)) return -1;
   hipLaunchKernelGGL(synth_rows_kernel, grid, dim3(256), 0, (hipStream_t)stream, *recipe, dtype, b0, t0, h0, nt, nh, n,
@@ -69,9 +70,10 @@ int synth_rows_device(const synth_row_recipe* recipe, int dtype, int b0, int nb,
 
 int synth_beta_device(uint32_t seed, int dtype, int b0, int nb, int t0, int nt, int h0, int nh, void* dst,
                       void* stream) {
-  if (!dst || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
+  if (nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
   uint64_t n = (uint64_t)nb * (uint64_t)nt * (uint64_t)nh;
   if (n == 0) return 0;
+  if (!dst) return -1;
   dim3 grid;
   if (synth_grid(n, &grid)) return -1;
   hipLaunchKernelGGL(synth_beta_kernel, grid, dim3(256), 0, (hipStream_t)stream, seed, dtype, b0, t0, h0, nt, nh, n,
@@ -81,9 +83,10 @@ int synth_beta_device(uint32_t seed, int dtype, int b0, int nb, int t0, int nt, 
 
 int synth_state_device(uint32_t seed, double scale, int dtype, int b0, int nb, int h0, int nh, void* dst,
                        void* stream) {
-  if (!dst || nb < 0 || nh < 0 || b0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
+  if (nb < 0 || nh < 0 || b0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
   uint64_t n = (uint64_t)nb * (uint64_t)nh * SYNTH_D;
   if (n == 0) return 0;
+  if (!dst) return -1;
   dim3 grid;
   if (synth_grid(n, &grid)) return -1;
   hipLaunchKernelGGL(synth_state_kernel, grid, dim3(256), 0, (hipStream_t)stream, seed, scale, dtype, b0, h0, nh, n,

@@ -77,7 +77,7 @@ static int synth_run(synth_job base, int64_t total, int n_threads) {
  * arguments. */
 int synth_rows_host(const synth_row_recipe* recipe, int dtype, int b0, int nb, int t0, int nt, int h0, int nh,
                     void* dst, int n_threads) {
-  if (!recipe || !dst || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
+  if (!recipe || (!dst && (int64_t)nb * nt * nh > 0) || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
   synth_job j = {0, recipe, 0, 0.0, dtype, b0, nb, t0, nt, h0, nh, dst, 0, 0};
   return synth_run(j, (int64_t)nb * nt * nh, n_threads);
 }
@@ -85,7 +85,9 @@ int synth_rows_host(const synth_row_recipe* recipe, int dtype, int b0, int nb, i
 /* beta for the same block into dst laid out [nb][nt][nh]. */
 int synth_beta_host(uint32_t seed, int dtype, int b0, int nb, int t0, int nt, int h0, int nh, void* dst,
                     int n_threads) {
-  if (!dst || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
+  if ((!dst && (int64_t)nb * nt * nh > 0) || nb < 0 || nt < 0 || nh < 0 || b0 < 0 || t0 < 0 || h0 < 0 || dtype < 0 ||
+      dtype > 2)
+    return -1;
   synth_job j = {1, NULL, seed, 0.0, dtype, b0, nb, t0, nt, h0, nh, dst, 0, 0};
   return synth_run(j, (int64_t)nb * nt * nh, n_threads);
 }
@@ -94,7 +96,7 @@ int synth_beta_host(uint32_t seed, int dtype, int b0, int nb, int t0, int nt, in
  * out [nb][nh][128][128]. */
 int synth_state_host(uint32_t seed, double scale, int dtype, int b0, int nb, int h0, int nh, void* dst,
                      int n_threads) {
-  if (!dst || nb < 0 || nh < 0 || b0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
+  if ((!dst && (int64_t)nb * nh > 0) || nb < 0 || nh < 0 || b0 < 0 || h0 < 0 || dtype < 0 || dtype > 2) return -1;
   synth_job j = {2, NULL, seed, scale, dtype, b0, nb, 0, 1, h0, nh, dst, 0, 0};
   return synth_run(j, (int64_t)nb * nh * SYNTH_D, n_threads);
 }

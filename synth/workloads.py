@@ -87,22 +87,26 @@ def host_inputs(w, b0=0, nb=None, t0=0, nt=None, h0=0, nh=None, dtype=None, thre
     return out
 
 
-def device_inputs(w, device="cuda", stream=None, T=None, seed=None):
-    """Draw all of workload w directly in device memory (torch tensors).
-    T overrides the sequence length (same streams, first T tokens)."""
+def device_inputs(w, device="cuda", stream=None, T=None, B=None, H=None, seed=None, dtype=None):
+    """Draw workload w directly in device memory (torch tensors).  B, T, H
+    override the shape (the first B sequences, T tokens, H heads of the same
+    streams); dtype overrides the I/O type ("bf16" or "f32")."""
     import torch
 
     from . import device_beta, device_rows, device_state
 
     s = w.seed if seed is None else seed
     T = w.T if T is None else T
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    dt = w.dtype if dtype is None else dtype
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     out = {}
     for name, r in recipes(w, s).items():
-        out[name] = device_rows(torch.empty((w.B, T, w.H, D), dtype=tdt, device=device), r, stream=stream)
-    out["beta"] = device_beta(torch.empty((w.B, T, w.H), dtype=torch.float32, device=device), s, stream=stream)
+        out[name] = device_rows(torch.empty((B, T, H, D), dtype=tdt, device=device), r, stream=stream)
+    out["beta"] = device_beta(torch.empty((B, T, H), dtype=torch.float32, device=device), s, stream=stream)
     out["s0"] = None
     if w.s0_scale is not None:
-        out["s0"] = device_state(torch.empty((w.B, w.H, D, D), dtype=torch.float32, device=device), s, w.s0_scale,
+        out["s0"] = device_state(torch.empty((B, H, D, D), dtype=torch.float32, device=device), s, w.s0_scale,
                                  stream=stream)
     return out

@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_23_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.fail("libkda.so is not built (run __graft_entry__.build())")
+    return kda.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error", "kda_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARGUMENT"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
+    assert lib.kda_version() >= 100
+
+
+# Fake, never-dereferenced device addresses: every case below fails validation
+# before anything is launched, so no GPU is touched.
+P = 0x10000
+MIS = 0x10008
+
+
+def chunk(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, initial_state=None, o=P, final_state=P, B=1, T=16, H=1, Dk=128, Dv=128,
+                dtype=kda.KDA_BF16)
+    args.update(kw)
+    return kda.raw_chunk_fwd(*args.values())
+
+
+def decode(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, state=P, o=P, B=1, H=1, Dk=128, Dv=128, dtype=kda.KDA_BF16)
+    args.update(kw)
+    return kda.raw_decode_step(*args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "a", "beta", "o", "final_state"])
+def test_chunk_rejects_null_pointers(lib, field):
+    assert chunk(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert field.split("_")[0] in kda.last_error()
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "a", "beta", "o", "final_state", "initial_state"])
+def test_chunk_rejects_misaligned_pointers(lib, field):
+    assert chunk(**{field: MIS}) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "aligned" in kda.last_error()
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "a", "beta", "state", "o"])
+def test_decode_rejects_null_and_misaligned(lib, field):
+    assert decode(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert decode(**{field: MIS}) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=-2), dict(Dk=0), dict(Dv=-128), dict(dtype=7)])
+def test_chunk_rejects_bad_sizes_and_enums(lib, kw):
+    assert chunk(**kw) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(Dk=64), dict(Dv=256), dict(Dk=96, Dv=96)])
+def test_unsupported_head_sizes(lib, kw):
+    assert chunk(**kw) == kda.KDA_ERR_UNSUPPORTED
+    assert decode(**kw) == kda.KDA_ERR_UNSUPPORTED
+    assert "128" in kda.last_error()
+
+
+def test_size_overflow_is_rejected(lib):
+    assert chunk(B=1 << 20, T=1 << 30, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert decode(B=1 << 20, H=1 << 20) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B * H == 0: nothing to do, nothing launched, NULL pointers allowed
+    assert kda.raw_chunk_fwd(None, None, None, None, None, None, None, None, 0, 16, 4, 128, 128, 0) == kda.KDA_OK
+    assert kda.raw_decode_step(None, None, None, None, None, None, None, 3, 0, 128, 128, 1) == kda.KDA_OK
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+
+    assert chunk(Dk=64) == kda.KDA_ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = kda.last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "128" in kda.last_error()
