@@ -1,7 +1,7 @@
 /*
  * kda_common.h -- device-side building blocks shared by the KDA kernels
  * (gfx950, wave64): element types, bf16 rounding, the gate of eq. (5), and
- * the 32x32 MFMA tile used for every dense contraction.
+ * the 16x16 MFMA tiles used for every dense contraction.
  */
 #pragma once
 
@@ -17,7 +17,7 @@ constexpr float kGateFloor = -5.0f;  // g_min of eq. (5)
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -30,97 +30,117 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
 
-/* Eq. (5) in base 2: g * log2(e) = -5 log2(e) sigmoid(a), using the hardware
- * exp2 and reciprocal (both within about one ulp). */
-__device__ __forceinline__ float gate_log2(float a) {
-  float e = __builtin_amdgcn_exp2f(-a * kLog2e);
-  return (kGateFloor * kLog2e) * __builtin_amdgcn_rcpf(1.0f + e);
+/* A loaded input element held in its own 32-bit register until it is used
+ * (bf16: the raw bits, zero-extended; fp32: the value). */
+template <typename IO>
+struct Raw;
+template <>
+struct Raw<bf16> {
+  typedef uint32_t type;
+  __device__ __forceinline__ static uint32_t load(const bf16* p, size_t i) {
+    return reinterpret_cast<const uint16_t*>(p)[i];
+  }
+  __device__ __forceinline__ static float f32(uint32_t x) { return __uint_as_float(x << 16); }
+};
+template <>
+struct Raw<float> {
+  typedef float type;
+  __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static float f32(float x) { return x; }
+};
+
+/* Eq. (5) in base 2 without the floor factor: sigmoid(a) via the hardware
+ * exp2 and reciprocal (each within about one ulp); g * log2(e) is
+ * (-5 log2 e) times this. */
+__device__ __forceinline__ float sigmoid_fast(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
 }
 
 /*
- * MFMA operands.  One K16 fragment is 8 values per lane covering a K = 16
- * slice of a contraction: lane l supplies row (A) or column (B) l % 32, and
- * its half l / 32 together with the slot s in 0..7 names the k index.  The
- * hardware pairs slot s of half h in A with slot s of half h in B, so any
- * fixed assignment of the 16 k indices to (h, s) gives the same product as
- * long as both operands use it.
+ * MFMA operands (16x16 tiles, wave64).  Lane l supplies row (A) or column
+ * (B) l % 16 of its operand; its group h = l / 16 and a slot index name the
+ * k index.  The hardware pairs slot s of group h in A with slot s of group h
+ * in B, so any fixed assignment of k indices to (h, s) gives the same
+ * product as long as both operands use it.
  *
- * The kernels use the assignment induced by the 32x32 accumulator layout
- * (lane l, register 4i + j holds row 8i + 4(l/32) + j of column l % 32): for a
- * block of 16 rows, slot s of half h is row kappa(h, s) = 8(s/4) + 4h + s%4.
- * With that assignment the first or last 8 accumulator registers of a tile
- * are directly a K16 fragment of the tile's rows, so a result can feed the
- * next contraction without moving data between lanes.
+ *   K = 16 fragments (4 slots):  k = 4h + s  -- the natural order, which is
+ *     also where the 16x16 accumulator keeps its rows (lane l, register j
+ *     holds row 4(l/16) + j of column l % 16), so a result feeds the next
+ *     contraction as its B operand without moving data between lanes.
+ *   K = 32 fragments (8 slots):  k = kappa(h, s) = 16 (s / 4) + 4 h + s % 4,
+ *     the rows that the accumulators of two stacked 16-row tiles put in lane
+ *     group h, again so that accumulators convert in place.
  */
-__host__ __device__ constexpr int kappa(int h, int s) { return 8 * (s / 4) + 4 * h + (s % 4); }
-__host__ __device__ constexpr int kappa_half(int r) { return (r / 4) % 2; }            // h with kappa(h, s) = r
-__host__ __device__ constexpr int kappa_slot(int r) { return 4 * (r / 8) + (r % 4); }  // s with kappa(h, s) = r
+__host__ __device__ constexpr int kappa(int h, int s) { return 16 * (s / 4) + 4 * h + (s % 4); }
+__host__ __device__ constexpr int kappa_group(int r) { return (r % 16) / 4; }          // h with kappa(h, s) = r
+__host__ __device__ constexpr int kappa_slot(int r) { return 4 * (r / 16) + (r % 4); }  // s with kappa(h, s) = r
 
 template <typename T>
-struct Frag;
+struct Frag8;  // K = 32 fragment
 template <>
-struct Frag<bf16> {
+struct Frag8<bf16> {
   bf16x8 v;
 };
 template <>
-struct Frag<float> {
+struct Frag8<float> {
   float v[8];
 };
-
-/* acc += A(32 x 16) * B(16 x 32) for one K16 fragment pair. */
-__device__ __forceinline__ void mfma_k16(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
-}
-__device__ __forceinline__ void mfma_k16(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[s], b.v[s], acc, 0, 0, 0);
-}
-
-/* Fragment from 8 consecutive accumulator registers acc[base .. base+7]. */
 template <typename T>
-__device__ __forceinline__ Frag<T> frag_from_acc(const f32x16& acc, int base);
+struct Frag4;  // K = 16 fragment
 template <>
-__device__ __forceinline__ Frag<bf16> frag_from_acc<bf16>(const f32x16& acc, int base) {
-  Frag<bf16> f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = (bf16)acc[base + s];
-  return f;
-}
+struct Frag4<bf16> {
+  bf16x4 v;
+};
 template <>
-__device__ __forceinline__ Frag<float> frag_from_acc<float>(const f32x16& acc, int base) {
-  Frag<float> f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = acc[base + s];
-  return f;
-}
+struct Frag4<float> {
+  float v[4];
+};
 
-template <typename T>
-__device__ __forceinline__ Frag<T> frag_from_f32(const float* x);
-template <>
-__device__ __forceinline__ Frag<bf16> frag_from_f32<bf16>(const float* x) {
-  Frag<bf16> f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = (bf16)x[s];
-  return f;
+/* acc(16x16) += A(16 x 32) B(32 x 16) */
+__device__ __forceinline__ void mfma_k32(f32x4& acc, const Frag8<bf16>& a, const Frag8<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
 }
-template <>
-__device__ __forceinline__ Frag<float> frag_from_f32<float>(const float* x) {
-  Frag<float> f;
+__device__ __forceinline__ void mfma_k32(f32x4& acc, const Frag8<float>& a, const Frag8<float>& b) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = x[s];
-  return f;
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+}
+/* acc(16x16) += A(16 x 16) B(16 x 16) */
+__device__ __forceinline__ void mfma_k16(f32x4& acc, const Frag4<bf16>& a, const Frag4<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_k16(f32x4& acc, const Frag4<float>& a, const Frag4<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
 }
 
 template <typename T>
-__device__ __forceinline__ Frag<T> frag_zero() {
-  float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  return frag_from_f32<T>(z);
+__device__ __forceinline__ Frag4<T> frag4(float x0, float x1, float x2, float x3) {
+  Frag4<T> f;
+  f.v[0] = from_f32<T>(x0);
+  f.v[1] = from_f32<T>(x1);
+  f.v[2] = from_f32<T>(x2);
+  f.v[3] = from_f32<T>(x3);
+  return f;
+}
+template <typename T>
+__device__ __forceinline__ Frag4<T> frag4(const f32x4& x) {
+  return frag4<T>(x[0], x[1], x[2], x[3]);
+}
+/* K = 32 fragment from two stacked accumulator tiles (rows 0..15, 16..31). */
+template <typename T>
+__device__ __forceinline__ Frag8<T> frag8(const f32x4& lo, const f32x4& hi) {
+  Frag8<T> f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f.v[s] = from_f32<T>(lo[s]);
+    f.v[4 + s] = from_f32<T>(hi[s]);
+  }
+  return f;
 }
 
-/* Load one K16 fragment (8 contiguous elements) from LDS. */
 template <typename T>
-__device__ __forceinline__ Frag<T> frag_load(const T* p) {
-  Frag<T> f;
+__device__ __forceinline__ Frag8<T> load_frag8(const T* p) {
+  Frag8<T> f;
   if constexpr (sizeof(T) == 2) {
     f.v = *reinterpret_cast<const bf16x8*>(p);
   } else {
@@ -133,6 +153,27 @@ __device__ __forceinline__ Frag<T> frag_load(const T* p) {
     }
   }
   return f;
+}
+template <typename T>
+__device__ __forceinline__ Frag4<T> load_frag4(const T* p) {
+  Frag4<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x4*>(p);
+  } else {
+    f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.v[s] = x[s];
+  }
+  return f;
+}
+template <typename T>
+__device__ __forceinline__ void store_frag4(T* p, const Frag4<T>& f) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(p) = f.v;
+  } else {
+    f32x4 x = {f.v[0], f.v[1], f.v[2], f.v[3]};
+    *reinterpret_cast<f32x4*>(p) = x;
+  }
 }
 
 }  // namespace kda
