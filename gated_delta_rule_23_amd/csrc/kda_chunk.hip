@@ -25,22 +25,27 @@
  * its group h = l/16 covers tokens 4h .. 4h+3 of a chunk.
  *   - The 128 x 128 fp32 state stays in MFMA accumulators for the whole
  *     sequence: each wave keeps 128 x 16 of it in eight 16x16 tiles.
- *   - Three chunks are in flight.  In iteration i:
- *       chain(i-2):  P = [Kh; Qh] S, [Vt; A Vt] = [M; A M] (V - Kh S),
- *                    O = Qh S + A Vt, S <- Diag(Gamma_C) S + Kb^T Vt
+ *   - Four chunks are in flight.  In iteration i:
+ *       chain(i-3):  P = [Kh; Qh] S, [Vt; A Vt] = [M; A M] (V - Kh S),
+ *                    O = Qh S + A Vt (stored straight from registers),
+ *                    S <- Diag(Gamma_C) S + Kb^T Vt
  *                    (18 MFMAs per wave, all waves, their own columns);
- *       inverse(i-1): one wave forms the 16x16 Gram products on MFMA and
- *                    (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) for the
- *                    nilpotent N = Diag(beta) L, also on MFMA;
+ *       solve(i-2):  one wave forms (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+ *                    for the nilpotent N = Diag(beta) L on MFMA, then M and A M;
+ *       gram(i-1):   another wave (on another SIMD) forms the 16x16 Gram
+ *                    products on MFMA and masks them into N and A;
  *       gate(i):     every lane: g = -5 sigmoid(a), cumulative sums, the four
  *                    scaled operands, written to LDS in MFMA fragment order;
- *       loads(i+1):  the next chunk's q, k, a, beta and V go to registers;
- *       store(i-3):  the output tile staged in LDS goes out in 16-byte rows.
+ *       loads:       the next gate's q, k, a, beta and the next chain's V go to
+ *                    registers through buffer loads sized to the chunk, which
+ *                    return zero past T.
  *     One workgroup barrier per iteration separates producers and consumers
- *     of the three LDS stages.
+ *     of the four LDS stages.
  * Contractions take bf16 operands with fp32 accumulation for bf16 I/O, and
  * fp32 operands (16x16x4 fp32 MFMA) for fp32 I/O.  The state stays fp32.
  */
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -48,25 +53,24 @@ namespace kda {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr float kGateLog2 = kGateFloor * kLog2e;  // g * log2(e) = kGateLog2 * sigmoid(a)
 
 /* One chunk's operands, in the order the MFMA lanes read them. */
 template <typename OT>
 struct Stage {
-  OT xf[2][4][64][8];  // [Kh | Qh][block of 32 key channels][lane][slot]: A of P = X S, and of the Gram products
-  OT kf[4][64][8];     // Kt: [block of 32 key channels][lane][slot]
-  OT kbf[8][64][4];    // Kb^T: [tile of 16 key channels][lane][token slot]: A of the state update
-  OT maf[2][64][4];    // [M | A M]: A of [Vt; A Vt] = [M; A M] R
-  float gamma_c[kD];   // Gamma_C per key channel
-  float beta[kChunk];
+  alignas(16) OT xf[2][4][64][8];  // [Kh | Qh][block of 32 key channels][lane][slot]: A of P = X S and of the Gram products
+  alignas(16) OT kf[4][64][8];     // Kt: [block of 32 key channels][lane][slot]
+  alignas(16) OT kbf[8][64][4];    // Kb^T: [tile of 16 key channels][lane][token slot]: A of the state update
+  alignas(16) OT maf[2][64][4];    // [M | A M]: A of [Vt; A Vt] = [M; A M] R
+  alignas(16) OT nf[3][64][4];     // N^T, N, A^T in C layout: operands of the solve
+  alignas(16) float gamma_c[kD];   // Gamma_C per key channel
+  alignas(16) float beta[kChunk];
 };
 
-template <typename IO, typename OT>
+template <typename OT>
 struct Smem {
   Stage<OT> st[kStages];
-  IO ostage[2][kChunk][kD];         // output tiles waiting for their coalesced store
-  float tscratch[kChunk][kChunk + 1];  // transpose scratch of the inverse
 };
 
 template <typename IO, typename OT>
@@ -75,20 +79,38 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
                                                              const float* __restrict__ beta,
                                                              const float* initial_state, IO* __restrict__ o,
                                                              float* final_state, int T, int H) {
-  __shared__ Smem<IO, OT> sm;
+  __shared__ Smem<OT> sm;
   const int unit = blockIdx.x;  // b * H + h
   const int bb = unit / H, hh = unit % H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, h = lane >> 4;
   const int col = 16 * wave + n;  // state column and key channel of this lane
-  const size_t rs = (size_t)H * kD;  // token stride of a row tensor
-  const size_t base = ((size_t)bb * T * H + hh) * kD;
   const int nchunks = (T + kChunk - 1) / kChunk;
 
-  // fragment coordinates of this lane's key channel inside the K = 32 blocks
-  const int kb_c = col >> 5;
-  const int grp_c = kappa_group(col & 31), slot_c = kappa_slot(col & 31);
+  // This (b, h) sequence: rows of token t start at seq + t * H * 128.
+  const int64_t tok_elems = (int64_t)H * kD;
+  const int64_t seq_off = ((int64_t)bb * T * H + hh) * kD;
+  const float* beta_seq = beta + (int64_t)bb * T * H + hh;
+  // Byte offsets of this lane's four tokens (4h .. 4h+3) inside a chunk.
+  int off_row[4], off_beta[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    off_row[j] = (int)(((4 * h + j) * tok_elems + col) * (int64_t)sizeof(IO));
+    off_beta[j] = (4 * h + j) * H * (int)sizeof(float);
+  }
+  // Chunk x of a row tensor / of beta as a buffer resource sized to the chunk's
+  // valid tokens: loads past T (or of chunks outside [0, nchunks)) return 0.
+  auto rows_rsrc = [&](const IO* base, int x) -> rsrc_t {
+    const int nval = (x < 0) ? 0 : min(kChunk, T - x * kChunk);
+    const int64_t bytes = nval > 0 ? ((int64_t)(nval - 1) * tok_elems + kD) * (int64_t)sizeof(IO) : 0;
+    return make_rsrc(base + seq_off + (int64_t)max(x, 0) * kChunk * tok_elems, bytes);
+  };
+  auto beta_rsrc = [&](int x) -> rsrc_t {
+    const int nval = (x < 0) ? 0 : min(kChunk, T - x * kChunk);
+    const int64_t bytes = nval > 0 ? ((int64_t)(nval - 1) * H + 1) * (int64_t)sizeof(float) : 0;
+    return make_rsrc(beta_seq + (int64_t)max(x, 0) * kChunk * H, bytes);
+  };
 
   // ---------------------------------------------------------------- state in
   f32x4 sacc[8];
@@ -100,52 +122,103 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       sacc[rt][j] = initial_state ? initial_state[((size_t)unit * kD + row) * kD + col] : 0.0f;
     }
 
-  // Registers carried between iterations: raw q, k, a, beta of the next gate
-  // pass and V of the next serial step.  Every iteration loads a chunk index
-  // clamped into range and a token clamped to T - 1, so the loads issue back
-  // to back with no branch; tokens past the end are masked where used.  Each
-  // element keeps its own 32-bit register until used, so no wait follows the
-  // loads: they complete under the next iteration's work.
-  typedef typename Raw<IO>::type RT;
-  RT rq[4], rk[4], ra[4], rv[4];
-  float rb[4];
-  auto load_raw = [&](int x, RT* lq, RT* lk, RT* la, float* lb) {
+  // Prefetch registers: q, k, a, beta of the next gate pass and V of the next
+  // serial step.  Two sets alternate between consecutive iterations, and every
+  // element keeps its own 32-bit register, so no wait follows the loads: they
+  // complete under the next iteration's work.
+  struct Regs {
+    uint32_t q[4], k[4], a[4], v[4];
+    float b[4];
+  };
+  auto load_gate_inputs = [&](int x, Regs& r) {
+    const rsrc_t rq = rows_rsrc(q, x), rk = rows_rsrc(k, x), ra = rows_rsrc(a, x), rb = beta_rsrc(x);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = min(x * kChunk + 4 * h + j, T - 1);
-      const size_t idx = base + (size_t)t * rs + col;
-      lq[j] = Raw<IO>::load(q, idx);
-      lk[j] = Raw<IO>::load(k, idx);
-      la[j] = Raw<IO>::load(a, idx);
-      lb[j] = beta[((size_t)bb * T + t) * H + hh];
+      r.q[j] = Raw<IO>::load(rq, off_row[j]);
+      r.k[j] = Raw<IO>::load(rk, off_row[j]);
+      r.a[j] = Raw<IO>::load(ra, off_row[j]);
+      r.b[j] = load_f32(rb, off_beta[j]);
     }
   };
-  auto load_v = [&](int x, RT* lv) {
+  auto load_chain_inputs = [&](int x, Regs& r) {
+    const rsrc_t rv = rows_rsrc(v, x);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = min(x * kChunk + 4 * h + j, T - 1);
-      lv[j] = Raw<IO>::load(v, base + (size_t)t * rs + col);
-    }
+    for (int j = 0; j < 4; ++j) r.v[j] = Raw<IO>::load(rv, off_row[j]);
   };
-  const int last = max(nchunks - 1, 0);
-  if (nchunks > 0) {
-    load_raw(0, rq, rk, ra, rb);
-    load_v(0, rv);
-  }
 
-  for (int i = 0; i < nchunks + 3; ++i) {
+  // Lanes n + 16 (h - 1), n + 16 (h - 2) and n + 48 of this channel, as byte
+  // addresses for ds_bpermute (loop-invariant).
+  const int addr_up1 = 4 * (lane >= 16 ? lane - 16 : lane);
+  const int addr_up2 = 4 * (lane >= 32 ? lane - 32 : lane);
+  const int addr_last = 4 * (n + 48);
+  // The 16x16 identity as a B operand.  A x I hands A back in accumulator
+  // layout, i.e. transposed across lanes: rows that sit one per lane (a key
+  // channel's four tokens) come back as four consecutive rows per lane, which
+  // is the order the MFMA fragments want.  The product is exact.
+  const Frag4<OT> ident = frag4<OT>(4 * h == n ? 1.0f : 0.0f, 4 * h + 1 == n ? 1.0f : 0.0f,
+                                    4 * h + 2 == n ? 1.0f : 0.0f, 4 * h + 3 == n ? 1.0f : 0.0f);
+  auto transpose16 = [&](const f32x4& x) {
+    f32x4 d = {0, 0, 0, 0};
+    mfma_k16(d, frag4<OT>(x), ident);
+    return frag4<OT>(d);
+  };
+
+  // ------------------------------------------------ gate: this lane's channel, tokens 4h .. 4h+3
+  auto gate = [&](const Regs& cur, Stage<OT>& st, int nvalid, auto ragged) {
+    float b[4];
+    float run = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float g2 = kGateLog2 * sigmoid_fast(Raw<IO>::f32(cur.a[j]));
+      if constexpr (decltype(ragged)::value) g2 = 4 * h + j < nvalid ? g2 : 0.0f;  // padded tokens: g = 0
+      run += g2;
+      b[j] = run;
+    }
+    // inclusive prefix over the four token groups of this channel
+    float u = run;
+    const float t1 = __int_as_float(__builtin_amdgcn_ds_bpermute(addr_up1, __float_as_int(u)));
+    u += h >= 1 ? t1 : 0.0f;
+    const float t2 = __int_as_float(__builtin_amdgcn_ds_bpermute(addr_up2, __float_as_int(u)));
+    u += h >= 2 ? t2 : 0.0f;
+    const float prefix = u - run;
+    const float bc = __int_as_float(__builtin_amdgcn_ds_bpermute(addr_last, __float_as_int(u)));  // log2 Gamma_C
+    const float gam_c = __builtin_amdgcn_exp2f(bc);
+    f32x4 kh, qh, kt, kbar;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float b2 = b[j] + prefix;
+      const float gam = __builtin_amdgcn_exp2f(b2);
+      const float inv = __builtin_amdgcn_exp2f(-b2);
+      const float kk = Raw<IO>::f32(cur.k[j]), qq = Raw<IO>::f32(cur.q[j]);  // zero past T
+      kh[j] = kk * gam;
+      qh[j] = qq * gam;
+      kt[j] = kk * inv;
+      kbar[j] = kt[j] * gam_c;
+    }
+    // After the transpose lane (token l%16, group h) holds key channels
+    // 16w + 4h .. 16w + 4h + 3: slots 0..3 (even w) or 4..7 (odd w) of its
+    // K = 32 fragment row in block w / 2.
+    const int kb_w = wave >> 1, so = 4 * (wave & 1);
+    store_frag4<OT>(&st.xf[0][kb_w][lane][so], transpose16(kh));
+    store_frag4<OT>(&st.xf[1][kb_w][lane][so], transpose16(qh));
+    store_frag4<OT>(&st.kf[kb_w][lane][so], transpose16(kt));
+    store_frag4<OT>(&st.kbf[wave][lane][0], frag4<OT>(kbar));  // already channel-major
+    if (h == 0) st.gamma_c[col] = gam_c;
+    if (n == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.beta[4 * h + j] = cur.b[j];  // zero past T
+    }
+  };
+
+  auto step = [&](int i, const Regs& cur, Regs& nxt) {
     // ------------------------------------------------ loads for the next iteration
-    RT nq[4], nk[4], na[4], nv[4];
-    float nb[4];
-    if (nchunks > 0) {
-      load_raw(min(i + 1, last), nq, nk, na, nb);
-      load_v(min(max(i - 1, 0), last), nv);
-    }
+    load_gate_inputs(i + 1, nxt);
+    load_chain_inputs(i - 2, nxt);
 
-    // ------------------------------------------------ chain(i - 2): the serial part
-    if (i - 2 >= 0 && i - 2 < nchunks) {
-      const int x = i - 2;
-      Stage<OT>& st = sm.st[x % kStages];
+    // ------------------------------------------------ chain(i - 3): the serial part
+    if (i - 3 >= 0 && i - 3 < nchunks) {
+      const int x = i - 3;
+      const Stage<OT>& st = sm.st[x % kStages];
       f32x4 pk = {0, 0, 0, 0}, pq = {0, 0, 0, 0};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -153,16 +226,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
         mfma_k32(pk, load_frag8<OT>(&st.xf[0][kb][lane][0]), sf);
         mfma_k32(pq, load_frag8<OT>(&st.xf[1][kb][lane][0]), sf);
       }
-      const int nvalid = min(kChunk, T - x * kChunk);
-      float rr[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rr[j] = (4 * h + j < nvalid ? Raw<IO>::f32(rv[j]) : 0.0f) - pk[j];
-      Frag4<OT> fr = frag4<OT>(rr[0], rr[1], rr[2], rr[3]);
+      // V is zero past T (and M has zero columns there), so padded tokens add nothing.
+      Frag4<OT> fr = frag4<OT>(Raw<IO>::f32(cur.v[0]) - pk[0], Raw<IO>::f32(cur.v[1]) - pk[1],
+                               Raw<IO>::f32(cur.v[2]) - pk[2], Raw<IO>::f32(cur.v[3]) - pk[3]);
       f32x4 dm = {0, 0, 0, 0}, da = {0, 0, 0, 0};
       mfma_k16(dm, load_frag4<OT>(&st.maf[0][lane][0]), fr);
       mfma_k16(da, load_frag4<OT>(&st.maf[1][lane][0]), fr);
+      // O rows 4h .. 4h+3 of this column; stores past T are dropped
+      const rsrc_t ro = rows_rsrc(o, x);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.ostage[x & 1][4 * h + j][col] = from_f32<IO>(pq[j] + da[j]);
+      for (int j = 0; j < 4; ++j) Raw<IO>::store(ro, off_row[j], pq[j] + da[j]);
       Frag4<OT> fv = frag4<OT>(dm);
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) {
@@ -172,10 +245,36 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       }
     }
 
-    // ------------------------------------------------ inverse(i - 1): one wave
-    if (i - 1 >= 0 && i - 1 < nchunks && wave == (i - 1) % kWaves) {
-      const int x = i - 1;
-      Stage<OT>& st = sm.st[x % kStages];
+    // ------------------------------------------------ solve(i - 2): one wave
+    if (i - 2 >= 0 && i - 2 < nchunks && wave == (i - 2) % kWaves) {
+      Stage<OT>& st = sm.st[(i - 2) % kStages];
+      const Frag4<OT> fnt = load_frag4<OT>(&st.nf[0][lane][0]);
+      const Frag4<OT> fnc = load_frag4<OT>(&st.nf[1][lane][0]);
+      const Frag4<OT> fat = load_frag4<OT>(&st.nf[2][lane][0]);
+      f32x4 y;  // Y0 = I - N
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (4 * h + j == n ? 1.0f : 0.0f) - to_f32(fnc.v[j]);
+      // A operand of X = C layout of X^T, so (N^p, (N^p)^T) pairs feed each other.
+      f32x4 n2c = {0, 0, 0, 0}, n2t = {0, 0, 0, 0}, n4c = {0, 0, 0, 0}, n4t = {0, 0, 0, 0}, n8t = {0, 0, 0, 0};
+      mfma_k16(n2c, fnt, fnc);
+      mfma_k16(n2t, fnc, fnt);
+      mfma_k16(y, frag4<OT>(n2t), frag4<OT>(y));  // Y1 = (I + N^2) Y0
+      mfma_k16(n4c, frag4<OT>(n2t), frag4<OT>(n2c));
+      mfma_k16(n4t, frag4<OT>(n2c), frag4<OT>(n2t));
+      mfma_k16(y, frag4<OT>(n4t), frag4<OT>(y));  // Y2 = (I + N^4) Y1
+      mfma_k16(n8t, frag4<OT>(n4c), frag4<OT>(n4t));
+      mfma_k16(y, frag4<OT>(n8t), frag4<OT>(y));  // (I + N)^{-1} = (I + N^8) Y2
+      const f32x4 m = y * st.beta[n];             // M = (I + N)^{-1} Diag(beta)
+      f32x4 am = {0, 0, 0, 0};
+      mfma_k16(am, fat, frag4<OT>(m));  // A M
+      // A fragments of [M; A M] = their accumulator layouts transposed
+      store_frag4<OT>(&st.maf[0][lane][0], transpose16(m));
+      store_frag4<OT>(&st.maf[1][lane][0], transpose16(am));
+    }
+
+    // ------------------------------------------------ gram(i - 1): another wave, another SIMD
+    if (i - 1 >= 0 && i - 1 < nchunks && wave == (i + 3) % kWaves) {
+      Stage<OT>& st = sm.st[(i - 1) % kStages];
       // C layouts (lane (n, h), register j <-> row r = 4h + j, column n):
       //   gkt = Kt Kh^T = (Kh Kt^T)^T,  gqt = Kt Qh^T = (Qh Kt^T)^T
       f32x4 gkt = {0, 0, 0, 0}, gqt = {0, 0, 0, 0};
@@ -192,114 +291,30 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
         int r = 4 * h + j;
         nt[j] = n > r ? bn * gkt[j] : 0.0f;
         at[j] = n >= r ? gqt[j] : 0.0f;
-        sm.tscratch[r][n] = nt[j];
       }
-      // lanes read each other's writes: order them explicitly within the wave
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      f32x4 nc, y;  // N, and Y0 = I - N
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        nc[j] = sm.tscratch[n][4 * h + j];
-        y[j] = (4 * h + j == n ? 1.0f : 0.0f) - nc[j];
-      }
-      // A operand of X = C layout of X^T, so (N^p, (N^p)^T) pairs feed each other.
-      f32x4 n2c = {0, 0, 0, 0}, n2t = {0, 0, 0, 0}, n4c = {0, 0, 0, 0}, n4t = {0, 0, 0, 0}, n8t = {0, 0, 0, 0};
-      mfma_k16(n2c, frag4<OT>(nt), frag4<OT>(nc));
-      mfma_k16(n2t, frag4<OT>(nc), frag4<OT>(nt));
-      mfma_k16(y, frag4<OT>(n2t), frag4<OT>(y));  // Y1 = (I + N^2) Y0
-      mfma_k16(n4c, frag4<OT>(n2t), frag4<OT>(n2c));
-      mfma_k16(n4t, frag4<OT>(n2c), frag4<OT>(n2t));
-      mfma_k16(y, frag4<OT>(n4t), frag4<OT>(y));  // Y2 = (I + N^4) Y1
-      mfma_k16(n8t, frag4<OT>(n4c), frag4<OT>(n4t));
-      mfma_k16(y, frag4<OT>(n8t), frag4<OT>(y));  // (I + N)^{-1} = (I + N^8) Y2
-      f32x4 m = y * bn;                           // M = (I + N)^{-1} Diag(beta)
-      f32x4 am = {0, 0, 0, 0};
-      mfma_k16(am, frag4<OT>(at), frag4<OT>(m));  // A M
-      // A fragments of [M; A M]: lane (row r, group n/4), slot n % 4
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int r = 4 * h + j;
-        st.maf[0][(n >> 2) * 16 + r][n & 3] = from_f32<OT>(m[j]);
-        st.maf[1][(n >> 2) * 16 + r][n & 3] = from_f32<OT>(am[j]);
-      }
+      store_frag4<OT>(&st.nf[0][lane][0], frag4<OT>(nt));
+      store_frag4<OT>(&st.nf[1][lane][0], transpose16(nt));  // C layout of N
+      store_frag4<OT>(&st.nf[2][lane][0], frag4<OT>(at));
     }
 
-    // ------------------------------------------------ gate(i): this lane's channel, tokens 4h .. 4h+3
+    // ------------------------------------------------ gate(i)
     if (i < nchunks) {
-      const int x = i;
-      Stage<OT>& st = sm.st[x % kStages];
-      const int nvalid = min(kChunk, T - x * kChunk);
-      float b[4], qm[4], km[4], bm[4];
-      float run = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = 4 * h + j < nvalid;  // padded tokens: g = 0, q = k = 0, beta = 0
-        float g2 = ok ? kGateLog2 * sigmoid_fast(Raw<IO>::f32(ra[j])) : 0.0f;
-        qm[j] = ok ? Raw<IO>::f32(rq[j]) : 0.0f;
-        km[j] = ok ? Raw<IO>::f32(rk[j]) : 0.0f;
-        bm[j] = ok ? rb[j] : 0.0f;
-        run += g2;
-        b[j] = run;
-      }
-      // prefix over the four token groups of this channel (lanes n, n+16, n+32, n+48)
-      float u = run;
-      float t1 = __shfl_up(u, 16, 64);
-      u += h >= 1 ? t1 : 0.0f;
-      float t2 = __shfl_up(u, 32, 64);
-      u += h >= 2 ? t2 : 0.0f;
-      const float prefix = u - run;
-      const float bc = __shfl(u, n + 48, 64);  // log2 of Gamma_C
-      const float gam_c = __builtin_amdgcn_exp2f(bc);
-      float kbar[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * h + j;
-        float b2 = b[j] + prefix;
-        float gam = __builtin_amdgcn_exp2f(b2);
-        float inv = __builtin_amdgcn_exp2f(-b2);
-        float kt = km[j] * inv;
-        const int fl = grp_c * 16 + r;
-        st.xf[0][kb_c][fl][slot_c] = from_f32<OT>(km[j] * gam);
-        st.xf[1][kb_c][fl][slot_c] = from_f32<OT>(qm[j] * gam);
-        st.kf[kb_c][fl][slot_c] = from_f32<OT>(kt);
-        kbar[j] = kt * gam_c;
-      }
-      store_frag4<OT>(&st.kbf[wave][lane][0], frag4<OT>(kbar[0], kbar[1], kbar[2], kbar[3]));
-      if (h == 0) st.gamma_c[col] = gam_c;
-      if (n == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st.beta[4 * h + j] = bm[j];
-      }
-    }
-
-    // ------------------------------------------------ store(i - 3): staged output tile
-    if (i - 3 >= 0 && i - 3 < nchunks && tid < 256) {
-      const int x = i - 3;
-      const int tok = tid >> 4, c8 = 8 * (tid & 15);
-      const int t = x * kChunk + tok;
-      if (t < T) {
-        const IO* src = &sm.ostage[x & 1][tok][c8];
-        IO* dst = o + base + (size_t)t * rs + c8;
-        if constexpr (sizeof(IO) == 2) {
-          *reinterpret_cast<bf16x8*>(dst) = *reinterpret_cast<const bf16x8*>(src);
-        } else {
-          reinterpret_cast<f32x4*>(dst)[0] = reinterpret_cast<const f32x4*>(src)[0];
-          reinterpret_cast<f32x4*>(dst)[1] = reinterpret_cast<const f32x4*>(src)[1];
-        }
-      }
+      const int nvalid = min(kChunk, T - i * kChunk);
+      Stage<OT>& st = sm.st[i % kStages];
+      if (nvalid == kChunk)
+        gate(cur, st, nvalid, std::false_type());
+      else
+        gate(cur, st, nvalid, std::true_type());
     }
 
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      rq[j] = nq[j];
-      rk[j] = nk[j];
-      ra[j] = na[j];
-      rb[j] = nb[j];
-      rv[j] = nv[j];
-    }
+  };
+
+  Regs A, B;
+  load_gate_inputs(0, A);
+  for (int i = 0; i < nchunks + 3; i += 2) {
+    step(i, A, B);
+    step(i + 1, B, A);
   }
 
   // ---------------------------------------------------------------- state out

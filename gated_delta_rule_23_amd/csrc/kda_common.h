@@ -19,6 +19,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
@@ -30,24 +31,46 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
 
+/*
+ * Buffer resources: a base address and a size in bytes, held in scalar
+ * registers.  Loads through them take a 32-bit per-lane byte offset and return
+ * zero beyond the size (stores there are dropped), so a chunk's loads need no
+ * 64-bit address arithmetic and no branch for a ragged tail.
+ */
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw, untyped 32-bit access (gfx9 family)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
 /* A loaded input element held in its own 32-bit register until it is used
- * (bf16: the raw bits, zero-extended; fp32: the value). */
+ * (bf16: the raw bits, zero-extended; fp32: the bits of the value). */
 template <typename IO>
 struct Raw;
 template <>
 struct Raw<bf16> {
-  typedef uint32_t type;
-  __device__ __forceinline__ static uint32_t load(const bf16* p, size_t i) {
-    return reinterpret_cast<const uint16_t*>(p)[i];
+  __device__ __forceinline__ static uint32_t load(rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
   }
   __device__ __forceinline__ static float f32(uint32_t x) { return __uint_as_float(x << 16); }
+  __device__ __forceinline__ static void store(rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)x), r, off, 0, 0);
+  }
 };
 template <>
 struct Raw<float> {
-  typedef float type;
-  __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
-  __device__ __forceinline__ static float f32(float x) { return x; }
+  __device__ __forceinline__ static uint32_t load(rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ __forceinline__ static float f32(uint32_t x) { return __uint_as_float(x); }
+  __device__ __forceinline__ static void store(rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+  }
 };
+__device__ __forceinline__ float load_f32(rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 
 /* Eq. (5) in base 2 without the floor factor: sigmoid(a) via the hardware
  * exp2 and reciprocal (each within about one ulp); g * log2(e) is
