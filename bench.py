@@ -34,7 +34,8 @@ STATE_BYTES = D * D * 4
 # Decode, per (sequence, head) step: state read + written once, q/k/v/a in, o out.
 DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + BYTES_PER_TOKEN_HEAD_BF16  # 132356
 
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+COPY_CALIBRATION_BYTES = 1 << 30  # one device-to-device copy of this many bytes (--calibrate-copy)
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
                   for n in ("kda_chunk.hip", "kda_common.h", "kda_decode.hip")]
 
@@ -47,18 +48,36 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, launch_bytes):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (lines "kernel=<name> kernel_source_sha=<sha> hbm_bytes_per_launch=<n>"),
+    or None when there is none or the kernel sources changed since."""
     try:
         with open(PROFILE_TRAFFIC) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            lines = f.readlines()
+    except OSError:
         return None
-    entry = rec.get(kernel)
-    if not entry or entry.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return entry.get("hbm_bytes_per_launch")
+    for line in lines:
+        fields = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
+        if fields.get("kernel") == kernel and fields.get("kernel_source_sha") == kernel_source_sha():
+            return float(fields["hbm_bytes_per_launch"])
+    return None
+
+
+def calibrate_copy():
+    """One plain device copy of COPY_CALIBRATION_BYTES (read once, written
+    once), outside any timed region: under rocprofv3 --pmc its FETCH_SIZE and
+    WRITE_SIZE scale the counters of the KDA kernels to bytes."""
+    import torch
+
+    n = COPY_CALIBRATION_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def timed_launches(fn, n, stream):
@@ -145,8 +164,9 @@ def bench_decode(reps=3):
 
 
 def cpu_baseline(threads):
-    """The oracle as it stands, on a bounded sample of the prefill workload:
-    16 of its 96 heads over all 8192 tokens, on `threads` host threads."""
+    """The oracle as it stands, on the prefill workload (all 96 heads, all
+    8192 tokens: about 30 core-seconds), on `threads` host threads.  Input
+    generation on the host is not timed."""
     import numpy as np
 
     import oracle
@@ -154,17 +174,16 @@ def cpu_baseline(threads):
     from synth.workloads import WORKLOADS, host_inputs
 
     w = WORKLOADS[1]
-    nh = 16
-    h = host_inputs(w, nh=nh, threads=threads)
+    h = host_inputs(w, threads=threads)
     args = (synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]), h["beta"].astype(np.float64))
     a = synth.to_f64(h["a"])
+    del h
     t0 = time.perf_counter()
     oracle.forward(*args, a=a, threads=threads)
     dt = time.perf_counter() - t0
-    token_heads = w.B * w.T * nh
-    return {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: heads 0-{nh - 1} of {w.H}, all {w.T} tokens ({token_heads} token-heads, "
-                      f"{dt:.2f} s); value scaled to tokens/s over all {w.H} heads"}
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {w.name} workload ({w.B * w.T * w.H} token-heads) in {dt:.2f} s, "
+                      f"fp64, one thread per (batch, head) sequence"}
 
 
 def main():
@@ -174,6 +193,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (every (batch, head) "
@@ -188,13 +209,15 @@ def main():
     import __graft_entry__
 
     __graft_entry__._ensure_built()
+    if args.calibrate_copy:
+        calibrate_copy()
 
     pre = bench_prefill(args.steps, args.warmup)
     w = pre["workload"]
     avg_s = pre["avg_ms"] / 1e3
     wall_per_step = pre["wall"] / args.steps
     achieved = pre["launch_bytes"] / avg_s
-    traffic = measured_traffic("chunk_fwd_kernel", pre["launch_bytes"])
+    traffic = measured_traffic("chunk_fwd_kernel")
     result = {
         "metric": METRIC,
         "value": pre["tokens"] / wall_per_step,
@@ -226,7 +249,7 @@ def main():
             "workload": dec["workload"].name, "value": dec["seq_steps_per_s"], "unit": "seq-steps/s",
             "steps": dec["steps"], "reps": dec["reps"], "ms_per_step": dec["avg_step_ms"],
             "roofline": {"bound": "hbm", "achieved": dach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK, "traffic": measured_traffic("decode_kernel", dec["step_bytes"]),
+                         "frac": dach / HBM_PEAK, "traffic": measured_traffic("decode_kernel"),
                          "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec["step_bytes"]},
         }
     if not args.no_cpu:
