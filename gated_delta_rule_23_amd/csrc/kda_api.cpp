@@ -25,6 +25,8 @@ kda_status fail(kda_status s, const char* fmt, ...) {
 
 kda_status ok() { return KDA_OK; }
 
+constexpr int kMaxPrefillHeads = 65536;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 /* Shared checks of dtype, head sizes and batch/head counts. */
@@ -62,6 +64,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
   if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
   const int64_t units = (int64_t)B * H;
   if (units == 0) return ok();
+  // a chunk of one tensor (16 tokens x H x 128 elements) is addressed with 32-bit byte offsets
+  if (H > kMaxPrefillHeads)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d exceeds the prefill limit of %d heads", fn, H, kMaxPrefillHeads);
   // every element index (b, t, h, channel) must fit in 63 bits: B*T*H*128 < 2^62
   if ((double)B * (double)T * (double)H * 128.0 > 4.0e18)
     return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*T*H*128 overflows the index range", fn);

@@ -71,6 +71,7 @@ struct Stage {
 template <typename OT>
 struct Smem {
   Stage<OT> st[kStages];
+  alignas(16) float prefix[kWaves][kChunk][4];  // per wave: [key channel][token group] partial sums of the gate
 };
 
 template <typename IO, typename OT>
@@ -99,18 +100,26 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     off_row[j] = (int)(((4 * h + j) * tok_elems + col) * (int64_t)sizeof(IO));
     off_beta[j] = (4 * h + j) * H * (int)sizeof(float);
   }
-  // Chunk x of a row tensor / of beta as a buffer resource sized to the chunk's
-  // valid tokens: loads past T (or of chunks outside [0, nchunks)) return 0.
-  auto rows_rsrc = [&](const IO* base, int x) -> rsrc_t {
-    const int nval = (x < 0) ? 0 : min(kChunk, T - x * kChunk);
-    const int64_t bytes = nval > 0 ? ((int64_t)(nval - 1) * tok_elems + kD) * (int64_t)sizeof(IO) : 0;
-    return make_rsrc(base + seq_off + (int64_t)max(x, 0) * kChunk * tok_elems, bytes);
-  };
-  auto beta_rsrc = [&](int x) -> rsrc_t {
-    const int nval = (x < 0) ? 0 : min(kChunk, T - x * kChunk);
-    const int64_t bytes = nval > 0 ? ((int64_t)(nval - 1) * H + 1) * (int64_t)sizeof(float) : 0;
-    return make_rsrc(beta_seq + (int64_t)max(x, 0) * kChunk * H, bytes);
-  };
+  // Chunk x of a row tensor / of beta as a buffer resource sized to the
+  // chunk's valid tokens: loads past T (or of chunks outside [0, nchunks))
+  // return 0 and stores there are dropped.  The sizes take three values and
+  // the bases advance by one chunk stride per iteration, so a descriptor costs
+  // a few scalar instructions.
+  const int64_t rows_step = (int64_t)kChunk * tok_elems * (int64_t)sizeof(IO);
+  const int64_t beta_step = (int64_t)kChunk * H * (int64_t)sizeof(float);
+  const int tail = T - (nchunks - 1) * kChunk;  // tokens in the last chunk (nchunks > 0)
+  const int rows_full = (int)(((kChunk - 1) * tok_elems + kD) * (int64_t)sizeof(IO));
+  const int rows_tail = (int)(((int64_t)(tail - 1) * tok_elems + kD) * (int64_t)sizeof(IO));
+  const int beta_full = ((kChunk - 1) * H + 1) * (int)sizeof(float);
+  const int beta_tail = ((tail - 1) * H + 1) * (int)sizeof(float);
+  auto rows_bytes = [&](int x) { return (unsigned)x < (unsigned)nchunks ? (x == nchunks - 1 ? rows_tail : rows_full) : 0; };
+  auto beta_bytes = [&](int x) { return (unsigned)x < (unsigned)nchunks ? (x == nchunks - 1 ? beta_tail : beta_full) : 0; };
+  const char* q_seq = reinterpret_cast<const char*>(q + seq_off);
+  const char* k_seq = reinterpret_cast<const char*>(k + seq_off);
+  const char* a_seq = reinterpret_cast<const char*>(a + seq_off);
+  const char* v_seq = reinterpret_cast<const char*>(v + seq_off);
+  const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
+  const char* b_seq = reinterpret_cast<const char*>(beta_seq);
 
   // ---------------------------------------------------------------- state in
   f32x4 sacc[8];
@@ -130,8 +139,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     uint32_t q[4], k[4], a[4], v[4];
     float b[4];
   };
-  auto load_gate_inputs = [&](int x, Regs& r) {
-    const rsrc_t rq = rows_rsrc(q, x), rk = rows_rsrc(k, x), ra = rows_rsrc(a, x), rb = beta_rsrc(x);
+  // x: chunk index; rows_off / beta_off: x chunk strides in bytes
+  auto load_gate_inputs = [&](int x, int64_t rows_off, int64_t beta_off, Regs& r) {
+    const int nb = rows_bytes(x);
+    const rsrc_t rq = make_rsrc(q_seq + rows_off, nb), rk = make_rsrc(k_seq + rows_off, nb),
+                 ra = make_rsrc(a_seq + rows_off, nb), rb = make_rsrc(b_seq + beta_off, beta_bytes(x));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       r.q[j] = Raw<IO>::load(rq, off_row[j]);
@@ -140,17 +152,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       r.b[j] = load_f32(rb, off_beta[j]);
     }
   };
-  auto load_chain_inputs = [&](int x, Regs& r) {
-    const rsrc_t rv = rows_rsrc(v, x);
+  auto load_chain_inputs = [&](int x, int64_t rows_off, Regs& r) {
+    const rsrc_t rv = make_rsrc(v_seq + rows_off, rows_bytes(x));
 #pragma unroll
     for (int j = 0; j < 4; ++j) r.v[j] = Raw<IO>::load(rv, off_row[j]);
   };
 
-  // Lanes n + 16 (h - 1), n + 16 (h - 2) and n + 48 of this channel, as byte
-  // addresses for ds_bpermute (loop-invariant).
-  const int addr_up1 = 4 * (lane >= 16 ? lane - 16 : lane);
-  const int addr_up2 = 4 * (lane >= 32 ? lane - 32 : lane);
-  const int addr_last = 4 * (n + 48);
   // The 16x16 identity as a B operand.  A x I hands A back in accumulator
   // layout, i.e. transposed across lanes: rows that sit one per lane (a key
   // channel's four tokens) come back as four consecutive rows per lane, which
@@ -174,15 +181,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       run += g2;
       b[j] = run;
     }
-    // inclusive prefix over the four token groups of this channel
-    float u = run;
-    const float t1 = __int_as_float(__builtin_amdgcn_ds_bpermute(addr_up1, __float_as_int(u)));
-    u += h >= 1 ? t1 : 0.0f;
-    const float t2 = __int_as_float(__builtin_amdgcn_ds_bpermute(addr_up2, __float_as_int(u)));
-    u += h >= 2 ? t2 : 0.0f;
-    const float prefix = u - run;
-    const float bc = __int_as_float(__builtin_amdgcn_ds_bpermute(addr_last, __float_as_int(u)));  // log2 Gamma_C
-    const float gam_c = __builtin_amdgcn_exp2f(bc);
+    // prefix over the four token groups of this channel, through LDS
+    float* pre = &sm.prefix[wave][n][0];
+    pre[h] = run;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // lanes read each other's writes
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const f32x4 part = *reinterpret_cast<const f32x4*>(pre);
+    const float prefix = (h > 0 ? part[0] : 0.0f) + (h > 1 ? part[1] : 0.0f) + (h > 2 ? part[2] : 0.0f);
+    const float gam_c = __builtin_amdgcn_exp2f((part[0] + part[1]) + (part[2] + part[3]));  // Gamma_C
     f32x4 kh, qh, kt, kbar;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -195,54 +202,76 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       kt[j] = kk * inv;
       kbar[j] = kt[j] * gam_c;
     }
-    // After the transpose lane (token l%16, group h) holds key channels
-    // 16w + 4h .. 16w + 4h + 3: slots 0..3 (even w) or 4..7 (odd w) of its
-    // K = 32 fragment row in block w / 2.
-    const int kb_w = wave >> 1, so = 4 * (wave & 1);
-    store_frag4<OT>(&st.xf[0][kb_w][lane][so], transpose16(kh));
-    store_frag4<OT>(&st.xf[1][kb_w][lane][so], transpose16(qh));
-    store_frag4<OT>(&st.kf[kb_w][lane][so], transpose16(kt));
+    // Transposes: afterwards lane (token l%16, group h) holds key channels
+    // 16w + 4h .. 16w + 4h + 3, i.e. slots 0..3 (even w) or 4..7 (odd w) of
+    // its K = 32 fragment row in block w / 2.  The three are independent.
+    f32x4 tkh = {0, 0, 0, 0}, tqh = {0, 0, 0, 0}, tkt = {0, 0, 0, 0};
+    mfma_k16(tkh, frag4<OT>(kh), ident);
+    mfma_k16(tqh, frag4<OT>(qh), ident);
+    mfma_k16(tkt, frag4<OT>(kt), ident);
     store_frag4<OT>(&st.kbf[wave][lane][0], frag4<OT>(kbar));  // already channel-major
     if (h == 0) st.gamma_c[col] = gam_c;
     if (n == 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st.beta[4 * h + j] = cur.b[j];  // zero past T
     }
+    const int kb_w = wave >> 1, so = 4 * (wave & 1);
+    store_frag4<OT>(&st.xf[0][kb_w][lane][so], frag4<OT>(tkh));
+    store_frag4<OT>(&st.xf[1][kb_w][lane][so], frag4<OT>(tqh));
+    store_frag4<OT>(&st.kf[kb_w][lane][so], frag4<OT>(tkt));
   };
 
+  // Byte offset of chunk i + 1 (rows and beta); chunk i + 1 - d is d strides lower.
+  int64_t rows_next = rows_step, beta_next = beta_step;
   auto step = [&](int i, const Regs& cur, Regs& nxt) {
     // ------------------------------------------------ loads for the next iteration
-    load_gate_inputs(i + 1, nxt);
-    load_chain_inputs(i - 2, nxt);
+    load_gate_inputs(i + 1, rows_next, beta_next, nxt);
+    load_chain_inputs(i - 2, rows_next - 3 * rows_step, nxt);
 
     // ------------------------------------------------ chain(i - 3): the serial part
     if (i - 3 >= 0 && i - 3 < nchunks) {
       const int x = i - 3;
       const Stage<OT>& st = sm.st[x % kStages];
-      f32x4 pk = {0, 0, 0, 0}, pq = {0, 0, 0, 0};
+      // operands from LDS first, so their latency hides behind the conversions
+      Frag8<OT> fk[4], fq[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        Frag8<OT> sf = frag8<OT>(sacc[2 * kb], sacc[2 * kb + 1]);
-        mfma_k32(pk, load_frag8<OT>(&st.xf[0][kb][lane][0]), sf);
-        mfma_k32(pq, load_frag8<OT>(&st.xf[1][kb][lane][0]), sf);
+        fk[kb] = load_frag8<OT>(&st.xf[0][kb][lane][0]);
+        fq[kb] = load_frag8<OT>(&st.xf[1][kb][lane][0]);
       }
+      const Frag4<OT> fm = load_frag4<OT>(&st.maf[0][lane][0]);
+      const Frag4<OT> fam = load_frag4<OT>(&st.maf[1][lane][0]);
+      Frag4<OT> fkb[8];
+      f32x4 gc[8];
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) {
+        fkb[rt] = load_frag4<OT>(&st.kbf[rt][lane][0]);
+        gc[rt] = *reinterpret_cast<const f32x4*>(&st.gamma_c[16 * rt + 4 * h]);
+      }
+      Frag8<OT> sf[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sf[kb] = frag8<OT>(sacc[2 * kb], sacc[2 * kb + 1]);
+      // Kh S first, so the residual is formed while Qh S runs
+      f32x4 pk = {0, 0, 0, 0}, pq = {0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mfma_k32(pk, fk[kb], sf[kb]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mfma_k32(pq, fq[kb], sf[kb]);
       // V is zero past T (and M has zero columns there), so padded tokens add nothing.
       Frag4<OT> fr = frag4<OT>(Raw<IO>::f32(cur.v[0]) - pk[0], Raw<IO>::f32(cur.v[1]) - pk[1],
                                Raw<IO>::f32(cur.v[2]) - pk[2], Raw<IO>::f32(cur.v[3]) - pk[3]);
       f32x4 dm = {0, 0, 0, 0}, da = {0, 0, 0, 0};
-      mfma_k16(dm, load_frag4<OT>(&st.maf[0][lane][0]), fr);
-      mfma_k16(da, load_frag4<OT>(&st.maf[1][lane][0]), fr);
+      mfma_k16(dm, fm, fr);
+      mfma_k16(da, fam, fr);
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) sacc[rt] *= gc[rt];  // Diag(Gamma_C) S, under the two MFMAs
+      const Frag4<OT> fv = frag4<OT>(dm);
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[rt], fkb[rt], fv);
       // O rows 4h .. 4h+3 of this column; stores past T are dropped
-      const rsrc_t ro = rows_rsrc(o, x);
+      const rsrc_t ro = make_rsrc(o_seq + rows_next - 4 * rows_step, rows_bytes(x));
 #pragma unroll
       for (int j = 0; j < 4; ++j) Raw<IO>::store(ro, off_row[j], pq[j] + da[j]);
-      Frag4<OT> fv = frag4<OT>(dm);
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt) {
-        f32x4 gc = *reinterpret_cast<const f32x4*>(&st.gamma_c[16 * rt + 4 * h]);
-        sacc[rt] *= gc;
-        mfma_k16(sacc[rt], load_frag4<OT>(&st.kbf[rt][lane][0]), fv);
-      }
     }
 
     // ------------------------------------------------ solve(i - 2): one wave
@@ -308,10 +337,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     }
 
     __syncthreads();
+    rows_next += rows_step;
+    beta_next += beta_step;
   };
 
   Regs A, B;
-  load_gate_inputs(0, A);
+  load_gate_inputs(0, 0, 0, A);
   for (int i = 0; i < nchunks + 3; i += 2) {
     step(i, A, B);
     step(i + 1, B, A);

@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARGUMENT = 1, /* NULL or misaligned pointer, negative size, overflow, bad enum */
-  KDA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement (Dk, Dv != 128) */
+  KDA_ERR_UNSUPPORTED = 2,      /* a valid request this library does not implement (Dk, Dv != 128; H > 65536 in prefill) */
   KDA_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
 } kda_status;
 
@@ -64,6 +64,8 @@ typedef enum {
  *   final_state    [B, H, Dk, Dv] fp32                       (written; may be the
  *                  same buffer as initial_state, any other overlap is undefined)
  *
+ * H is at most 65536 (one chunk of one tensor must span less than 2^31
+ * bytes); larger H fails with KDA_ERR_UNSUPPORTED.
  * T need not be a multiple of 16: the last chunk is partial, with the same
  * result as padding it with tokens of beta = 0, g = 0 and q = 0.  T = 0 copies
  * initial_state (or zeros) into final_state; q, k, v, a, beta and o may then

@@ -93,6 +93,12 @@ def test_unsupported_head_sizes(lib, kw):
     assert "128" in kda.last_error()
 
 
+def test_prefill_head_limit(lib):
+    # a chunk of one tensor must stay under 2^31 bytes for 32-bit buffer offsets
+    assert chunk(H=65537) == kda.KDA_ERR_UNSUPPORTED
+    assert "65536" in kda.last_error()
+
+
 def test_size_overflow_is_rejected(lib):
     assert chunk(B=1 << 20, T=1 << 30, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT
     assert decode(B=1 << 20, H=1 << 20) == kda.KDA_ERR_INVALID_ARGUMENT
