@@ -35,9 +35,10 @@ STATE_BYTES = D * D * 4
 DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + BYTES_PER_TOKEN_HEAD_BF16  # 132356
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+PREFILL_KERNEL = "chunk_fwd_bf16_kernel"  # the kernel the bf16 prefill workload runs
 COPY_CALIBRATION_BYTES = 1 << 30  # one device-to-device copy of this many bytes (--calibrate-copy)
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
-                  for n in ("kda_chunk.hip", "kda_common.h", "kda_decode.hip")]
+                  for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_common.h", "kda_decode.hip")]
 
 
 def kernel_source_sha():
@@ -217,7 +218,7 @@ def main():
     avg_s = pre["avg_ms"] / 1e3
     wall_per_step = pre["wall"] / args.steps
     achieved = pre["launch_bytes"] / avg_s
-    traffic = measured_traffic("chunk_fwd_kernel")
+    traffic = measured_traffic(PREFILL_KERNEL)
     result = {
         "metric": METRIC,
         "value": pre["tokens"] / wall_per_step,
@@ -235,7 +236,7 @@ def main():
                    "io": "bf16 q/k/v/a/o, fp32 beta and state", "seed": w.seed},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
-                     "kernel": "chunk_fwd_kernel", "launch_ms": pre["avg_ms"],
+                     "kernel": PREFILL_KERNEL, "launch_ms": pre["avg_ms"],
                      "algorithmic_bytes_per_launch": pre["launch_bytes"]},
         "mfma": {"algorithmic_flops_per_launch": pre["launch_flops"],
                  "achieved_tflops": pre["launch_flops"] / avg_s / 1e12,

@@ -1,5 +1,6 @@
 /*
- * kda_chunk.hip -- chunkwise KDA prefill on gfx950.
+ * kda_chunk.hip -- chunkwise KDA prefill on gfx950: the general kernel, used
+ * for fp32 I/O (bf16 I/O has its own kernel in kda_prefill_bf16.hip).
  *
  * The method (page "Kimi K3：从三条信息流到完整系统", wineandchord.com).
  * Per (batch, head) the sequence is cut into chunks of C = 16 tokens.  With S
@@ -124,12 +125,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   // ---------------------------------------------------------------- state in
   f32x4 sacc[8];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
+  for (int rt = 0; rt < 8; ++rt) sacc[rt] = f32x4{0, 0, 0, 0};
+  if (initial_state) {  // one test, so the loads issue back to back
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int row = 16 * rt + 4 * h + j;
-      sacc[rt][j] = initial_state ? initial_state[((size_t)unit * kD + row) * kD + col] : 0.0f;
-    }
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sacc[rt][j] = initial_state[((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + col];
+  }
 
   // Prefetch registers: q, k, a, beta of the next gate pass and V of the next
   // serial step.  Two sets alternate between consecutive iterations, and every
@@ -364,9 +366,7 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
   const int units = B * H;
   if (units == 0) return hipSuccess;
   if (bf16_io) {
-    hipLaunchKernelGGL((chunk_fwd_kernel<bf16, bf16>), dim3(units), dim3(kThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
-                       H);
+    return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream);
   } else {
     hipLaunchKernelGGL((chunk_fwd_kernel<float, float>), dim3(units), dim3(kThreads), 0, stream, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state,

@@ -147,16 +147,27 @@ __device__ __forceinline__ Frag4<T> frag4(float x0, float x1, float x2, float x3
 }
 template <typename T>
 __device__ __forceinline__ Frag4<T> frag4(const f32x4& x) {
-  return frag4<T>(x[0], x[1], x[2], x[3]);
+  if constexpr (sizeof(T) == 2) {
+    Frag4<T> f;
+    f.v = __builtin_convertvector(x, bf16x4);  // two packed conversions
+    return f;
+  } else {
+    return frag4<T>(x[0], x[1], x[2], x[3]);
+  }
 }
 /* K = 32 fragment from two stacked accumulator tiles (rows 0..15, 16..31). */
 template <typename T>
 __device__ __forceinline__ Frag8<T> frag8(const f32x4& lo, const f32x4& hi) {
   Frag8<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4), 0, 1, 2,
+                                  3, 4, 5, 6, 7);
+  } else {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f.v[s] = from_f32<T>(lo[s]);
-    f.v[4 + s] = from_f32<T>(hi[s]);
+    for (int s = 0; s < 4; ++s) {
+      f.v[s] = lo[s];
+      f.v[4 + s] = hi[s];
+    }
   }
   return f;
 }

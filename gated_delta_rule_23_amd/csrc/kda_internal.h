@@ -13,9 +13,14 @@ namespace kda {
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
                          void* o, int units, bool bf16_io, hipStream_t stream);
 
-/* Chunkwise prefill over [B, T, H, 128] rows. */
+/* Chunkwise prefill over [B, T, H, 128] rows: fp32 or bf16 I/O (kda_chunk.hip). */
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             const float* initial_state, void* o, float* final_state, int B, int T, int H,
                             bool bf16_io, hipStream_t stream);
+
+/* The bf16 I/O prefill (kda_prefill_bf16.hip); launch_chunk_fwd dispatches to it. */
+hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                 const float* initial_state, void* o, float* final_state, int B, int T, int H,
+                                 hipStream_t stream);
 
 }  // namespace kda

@@ -1,0 +1,428 @@
+/*
+ * kda_prefill_bf16.hip -- chunkwise KDA prefill for bf16 q, k, v, a, o on gfx950.
+ *
+ * Same chunk algebra as the general kernel in kda_chunk.hip (page "Kimi
+ * K3：从三条信息流到完整系统", eq. (1), (3), (4), (5)); per chunk of C = 16
+ * tokens, with b the in-chunk cumulative log-decay and Gamma = e^b:
+ *   Kh = K Gamma, Qh = Q Gamma, Kt = K / Gamma, Kb = K Gamma_C / Gamma,
+ *   N  = Diag(beta) StrictTril(Kh Kt^T),  A = Tril(Qh Kt^T),
+ *   M  = (I + N)^{-1} Diag(beta),  W = M Kh,  U = M V,
+ *   Vt = U - W S,   O = Qh S + A Vt,   S' = Diag(Gamma_C) S + Kb^T Vt.
+ * Folding M into W and U before the state arrives leaves three MFMA rounds
+ * on the serial path (W S and Qh S, then A Vt and the state update).
+ *
+ * Mapping: one 512-thread workgroup per (b, h), 8 waves, two per SIMD: wave
+ * c < 4 (the chain wave of SIMD c) owns state columns 32c .. 32c+31 (sixteen
+ * 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD g)
+ * owns key channels 32g .. 32g+31 of the per-chunk work, so every SIMD pairs
+ * the MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the
+ * main loop does, separated by one workgroup barrier:
+ *   gate waves:  loads of chunk i+2 (gate wave g: tensor g of q, k, a, v,
+ *                16-byte buffer loads of 256-byte rows), staged to LDS
+ *                token-major one iteration later; gate(i): lane (channel,
+ *                tokens 4(l/16) .. +3): g, the cumulative sums and the four
+ *                scaled operands, stored channel-major; gram(i-1) on one wave:
+ *                Kt Kh^T and Kt Qh^T masked into N and A; solve(i-2) on
+ *                another: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+ *                (N is nilpotent, the product is exact) and M;
+ *   chain waves: prep(i-3): their tiles of W = M Kh and U = M V;
+ *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
+ *                S <- Diag(Gamma_C) S + Kb^T Vt.
+ * Operands change between token-major and channel-major through
+ * ds_read_b64_tr_b16, which transposes 16-bit elements across the lanes of
+ * each 16-lane group while it reads: lane i, element j of the result is
+ * element i % 4 of what lane 4j + i/4 addressed.  A 16-row tile with rows of
+ * 16 elements read at byte 8 * lane thus arrives with lane i holding column
+ * i, rows 4(l/16) .. +3 -- the accumulator (and B operand) layout -- while a
+ * plain 8-byte read of row i, elements 4(l/16) .. +3 gives the A layout.
+ */
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 32 state columns each
+constexpr int kThreads = 64 * 2 * kChainWaves;  // plus one gate wave per SIMD
+constexpr int kPadRow = 144;  // staged input row: 128 channels + 16 pad (288 B: the 4 rows a 16-lane group reads hit distinct banks)
+constexpr float kGateLog2 = kGateFloor * kLog2e;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+/* LDS rings.  A chunk x lives in slot x % (ring size) of each ring; the sizes
+ * follow from the iteration that writes it and the last one that reads it. */
+struct Smem {
+  alignas(16) bf16 qka[2][3][kChunk][kPadRow];  // q, k, a, token-major: staged at i-1, read by gate(i)
+  alignas(16) bf16 vin[5][kChunk][kPadRow];     // v, token-major: staged at x-1, read by prep(x) at x+3
+  alignas(16) bf16 kh[4][kD][kChunk];           // channel-major [channel][token]: gram (x+1), prep (x+3)
+  alignas(16) bf16 qh[5][kD][kChunk];           // gram (x+1), chain (x+4)
+  alignas(16) bf16 kt[2][kD][kChunk];           // gram (x+1)
+  alignas(16) bf16 kb[5][kD][kChunk];           // chain (x+4)
+  alignas(16) bf16 w[2][kD][kChunk];            // written by prep (x+3), read by chain (x+4)
+  alignas(16) bf16 n[2][kChunk][kChunk];        // N, row-major: gram (x+1) -> solve (x+2)
+  alignas(16) bf16 am[5][kChunk][kChunk];       // A, row-major: gram (x+1) -> chain (x+4)
+  alignas(16) bf16 mt[2][kChunk][kChunk];       // M^T, row-major: solve (x+2) -> prep (x+3)
+  alignas(16) float gamma_c[5][4][4][8];        // Gamma_C[16 rt + 4 g + q] at [g][q][rt]: gate (x) -> chain (x+4)
+  alignas(16) float beta[4][kChunk];            // staged at x-1 -> solve (x+2)
+  alignas(16) bf16 ost[kChainWaves][2][kChunk][kChunk];  // per chain wave and column tile: O, [column][token]
+  alignas(16) float prefix[kChainWaves][2][kChunk][4];    // per gate wave and channel tile: gate partial sums
+};
+
+__device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+__device__ __forceinline__ bf16x4 lds_b64(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ void lds_put(bf16* p, const f32x4& x) {
+  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(x, bf16x4);
+}
+__device__ __forceinline__ f32x4 bf16x4_to_f32(bf16x4 b) {
+  const u32x2 u = __builtin_bit_cast(u32x2, b);
+  f32x4 r = {__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+             __uint_as_float(u[1] & 0xffff0000u)};
+  return r;
+}
+__device__ __forceinline__ Frag8<bf16> cat8(bf16x4 lo, bf16x4 hi) {
+  Frag8<bf16> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ Frag4<bf16> f4(bf16x4 x) {
+  Frag4<bf16> f;
+  f.v = x;
+  return f;
+}
+/* The value of lane J of this lane's quad (DPP quad permutation). */
+template <int J>
+__device__ __forceinline__ float quad_bcast(float x) {
+  constexpr int ctrl = J | (J << 2) | (J << 4) | (J << 6);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, true));  // folds into the user
+}
+/* Orders LDS accesses of the lanes of one wave (a write, then reads of it by other lanes). */
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+/* Workgroup barrier.  The chain and gate waves run separate loops, each with
+ * exactly one of these per iteration and one before the loop. */
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
+                                                                  const bf16* __restrict__ k,
+                                                                  const bf16* __restrict__ v,
+                                                                  const bf16* __restrict__ a,
+                                                                  const float* __restrict__ beta,
+                                                                  const float* initial_state, bf16* __restrict__ o,
+                                                                  float* final_state, int T, int H) {
+  __shared__ Smem sm;
+  const int unit = blockIdx.x;  // b * H + h
+  const int bb = unit / H, hh = unit % H;
+  // The wave index is uniform; saying so keeps everything derived from it
+  // (buffer resources, branch conditions) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, h = lane >> 4;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  // Iterations of the main loop (both wave kinds, an even count): chunk x
+  // passes gate at x, gram at x+1, solve at x+2, prep at x+3, chain at x+4.
+  const int nsteps = (nchunks + 5) & ~1;
+
+  // ---------------------------------------------------------------- addressing
+  // Token t of this sequence starts tok_bytes * t bytes into its tensor.  A
+  // chunk is a buffer resource sized to its valid tokens (loads past T return
+  // 0, stores there are dropped; chunks outside [0, nchunks) have size 0).
+  const int64_t seq_off = ((int64_t)bb * T * H + hh) * kD;
+  const int tok_bytes = H * kD * (int)sizeof(bf16);
+  const int64_t rows_step = (int64_t)kChunk * tok_bytes;
+  const int64_t beta_step = (int64_t)kChunk * H * (int64_t)sizeof(float);
+  const int tail = T - (nchunks - 1) * kChunk;
+  const int rows_full = (kChunk - 1) * tok_bytes + kD * (int)sizeof(bf16);
+  const int rows_tail = (tail - 1) * tok_bytes + kD * (int)sizeof(bf16);
+  const int beta_full = ((kChunk - 1) * H + 1) * (int)sizeof(float);
+  const int beta_tail = ((tail - 1) * H + 1) * (int)sizeof(float);
+  auto rows_bytes = [&](int x) { return (unsigned)x < (unsigned)nchunks ? (x == nchunks - 1 ? rows_tail : rows_full) : 0; };
+  auto beta_bytes = [&](int x) { return (unsigned)x < (unsigned)nchunks ? (x == nchunks - 1 ? beta_tail : beta_full) : 0; };
+
+  if (wave < kChainWaves) {
+    // ================================================================ chain wave c: columns 32c .. 32c+31
+    const int c = wave;
+    const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
+    f32x4 sacc[2][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][32c + 16 ct + l%16]
+    const bool has_s0 = initial_state != nullptr;  // one test, so the loads below issue back to back
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[ct][rt][j] = 0.0f;
+    if (has_s0) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sacc[ct][rt][j] = initial_state[((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + 32 * c + 16 * ct + n];
+    }
+    f32x4 u[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};  // U tiles of the chunk whose chain runs next
+
+    // ------------------------------------------------------------ prep(x): W and U tiles
+    auto prep = [&](int x) {
+      const Frag4<bf16> fm = f4(lds_tr(&sm.mt[x & 1][0][0] + 4 * lane));  // A layout of M
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int ch = 32 * c + 16 * ct + n;
+        // B layouts of Kh (channels 32c + 16ct ..) and of V (columns 32c + 16ct ..)
+        const Frag4<bf16> fkh = f4(lds_b64(&sm.kh[x & 3][0][0] + ch * kChunk + 4 * h));
+        const Frag4<bf16> fv =
+            f4(lds_tr(&sm.vin[x % 5][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * c + 16 * ct + 4 * (n & 3)));
+        f32x4 wc = {0, 0, 0, 0}, uc = {0, 0, 0, 0};
+        mfma_k16(wc, fm, fkh);
+        mfma_k16(uc, fm, fv);
+        lds_put(&sm.w[x & 1][0][0] + ch * kChunk + 4 * h, wc);  // channel-major W
+        u[ct] = uc;
+      }
+    };
+
+    // ------------------------------------------------------------ chain(x): the serial part
+    auto chain = [&](int x) {
+      const bf16* tw = &sm.w[x & 1][0][0];
+      const bf16* tq = &sm.qh[x % 5][0][0];
+      const bf16* tb = &sm.kb[x % 5][0][0];
+      Frag8<bf16> fw[4], fq[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int lo = 32 * kb * kChunk + 4 * lane, hi = lo + 16 * kChunk;
+        fw[kb] = cat8(lds_tr(tw + lo), lds_tr(tw + hi));
+        fq[kb] = cat8(lds_tr(tq + lo), lds_tr(tq + hi));
+      }
+      const Frag4<bf16> fa = f4(lds_b64(&sm.am[x % 5][0][0] + n * kChunk + 4 * h));  // A layout of A
+      Frag4<bf16> fkb[8];
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) fkb[rt] = f4(lds_b64(tb + (16 * rt + n) * kChunk + 4 * h));  // A layout of Kb^T
+      // Gamma_C[16 rt + 4h + l%4] for all rt; row 16 rt + 4h + j comes from lane j of the quad
+      const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.gamma_c[x % 5][h][n & 3][0]);
+      const f32x4 g_lo = gp[0], g_hi = gp[1];
+      f32x4 pw[2], pq[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        Frag8<bf16> sf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sf[kb] = frag8<bf16>(sacc[ct][2 * kb], sacc[ct][2 * kb + 1]);
+        pw[ct] = f32x4{0, 0, 0, 0};
+        pq[ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mfma_k32(pw[ct], fw[kb], sf[kb]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mfma_k32(pq[ct], fq[kb], sf[kb]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        // Diag(Gamma_C) S, under the MFMAs above
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+          const float g = rt < 4 ? g_lo[rt] : g_hi[rt - 4];
+          sacc[ct][rt][0] *= quad_bcast<0>(g);
+          sacc[ct][rt][1] *= quad_bcast<1>(g);
+          sacc[ct][rt][2] *= quad_bcast<2>(g);
+          sacc[ct][rt][3] *= quad_bcast<3>(g);
+        }
+        // Vt = U - W S (zero for padded tokens: U and W have zero rows there)
+        const Frag4<bf16> fv = frag4<bf16>(u[ct] - pw[ct]);
+        f32x4 da = {0, 0, 0, 0};
+        mfma_k16(da, fa, fv);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[ct][rt], fkb[rt], fv);
+        // O = Qh S + A Vt, through this wave's LDS tile to token-major rows
+        bf16* ot = &sm.ost[c][ct][0][0];
+        lds_put(ot + n * kChunk + 4 * h, pq[ct] + da);
+        wave_lds_sync();
+        const bf16x4 orow = lds_tr(ot + 4 * lane);  // token l%16, columns 32c + 16ct + 4h .. +3
+        const rsrc_t ro = make_rsrc(o_seq + x * rows_step, rows_bytes(x));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, orow), ro,
+                                              n * tok_bytes + (32 * c + 16 * ct + 4 * h) * (int)sizeof(bf16), 0, 0);
+      }
+    };
+
+    block_sync();  // inputs of chunk 0 staged
+    for (int i = 0; i < nsteps; ++i) {
+      if (i >= 4 && i - 4 < nchunks) chain(i - 4);
+      if (i >= 3 && i - 3 < nchunks) prep(i - 3);
+      block_sync();
+    }
+
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t idx = ((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + 32 * c + 16 * ct + n;
+          final_state[idx] = sacc[ct][rt][j];
+        }
+  } else {
+    // ================================================================ gate wave g: key channels 32g .. 32g+31
+    const int g = wave - kChainWaves;
+    // Loads: gate wave g stages tensor g (q, k, a, v), rows 4h .. 4h+3,
+    // 16 bytes (channels 8(l%16) .. +7) each; gate wave 0 also beta.
+    const char* ld_seq = reinterpret_cast<const char*>((g == 0 ? q : g == 1 ? k : g == 2 ? a : v) + seq_off);
+    const int ld_off = 4 * h * tok_bytes + 16 * n;
+    const char* beta_seq = reinterpret_cast<const char*>(beta + (int64_t)bb * T * H + hh);
+    const int beta_off = n * H * (int)sizeof(float);
+    struct Staged {
+      u32x4 r[4];  // rows 4h .. 4h+3
+      float b;     // beta of token l%16 (gate wave 0)
+    };
+    auto load_chunk = [&](int x, Staged& st) {
+      const rsrc_t r = make_rsrc(ld_seq + x * rows_step, rows_bytes(x));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off + j * tok_bytes, 0, 0);
+      if (g == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, beta_bytes(x)), beta_off);
+    };
+    auto stage_chunk = [&](int x, const Staged& st) {
+      bf16* dst = g < 3 ? &sm.qka[x & 1][g][0][0] : &sm.vin[x % 5][0][0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + (4 * h + j) * kPadRow + 8 * n) = st.r[j];
+      if (g == 0 && h == 0) sm.beta[x & 3][n] = st.b;
+    };
+
+    // -------------------------------------------------------------- gate(x)
+    auto gate = [&](int x, auto ragged) {
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        const int ch = 32 * g + 16 * cs + n;  // this lane's channel; tokens 4h .. 4h+3
+        // Lane (l%16, h) addresses row 4h + (l%16)/4, elements 32g + 16cs + 4(l%4) ..;
+        // the transposing read returns channel ch, tokens 4h .. 4h+3.
+        const bf16* in = &sm.qka[x & 1][0][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * g + 16 * cs + 4 * (n & 3);
+        const f32x4 qq = bf16x4_to_f32(lds_tr(in));
+        const f32x4 kk = bf16x4_to_f32(lds_tr(in + kChunk * kPadRow));
+        const f32x4 aa = bf16x4_to_f32(lds_tr(in + 2 * kChunk * kPadRow));
+        float b[4];
+        float run = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float g2 = kGateLog2 * sigmoid_fast(aa[j]);
+          if constexpr (decltype(ragged)::value) g2 = x * kChunk + 4 * h + j < T ? g2 : 0.0f;  // padded tokens: g = 0
+          run += g2;
+          b[j] = run;
+        }
+        float* pre = &sm.prefix[g][cs][n][0];
+        pre[h] = run;
+        wave_lds_sync();
+        const f32x4 part = *reinterpret_cast<const f32x4*>(pre);
+        const float prefix = (h > 0 ? part[0] : 0.0f) + (h > 1 ? part[1] : 0.0f) + (h > 2 ? part[2] : 0.0f);
+        const float gam_c = __builtin_amdgcn_exp2f((part[0] + part[1]) + (part[2] + part[3]));
+        f32x4 kh, qh, kt, kb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float b2 = b[j] + prefix;
+          const float gam = __builtin_amdgcn_exp2f(b2);
+          const float inv = __builtin_amdgcn_exp2f(-b2);
+          kh[j] = kk[j] * gam;
+          qh[j] = qq[j] * gam;
+          kt[j] = kk[j] * inv;
+          kb[j] = kt[j] * gam_c;
+        }
+        const int cm = ch * kChunk + 4 * h;  // [channel][token] element offset
+        lds_put(&sm.kh[x & 3][0][0] + cm, kh);
+        lds_put(&sm.qh[x % 5][0][0] + cm, qh);
+        lds_put(&sm.kt[x & 1][0][0] + cm, kt);
+        lds_put(&sm.kb[x % 5][0][0] + cm, kb);
+        if (h == 0) sm.gamma_c[x % 5][n >> 2][n & 3][2 * g + cs] = gam_c;
+      }
+    };
+
+    // -------------------------------------------------------------- gram(x): one wave
+    auto gram = [&](int x) {
+      const bf16* tkt = &sm.kt[x & 1][0][0];
+      const bf16* tkh = &sm.kh[x & 3][0][0];
+      const bf16* tqh = &sm.qh[x % 5][0][0];
+      // C layouts: gkt = Kt Kh^T, lane (token c, h), register j <-> token r = 4h + j:
+      // (Kh Kt^T)[c][r]; likewise gqt holds (Qh Kt^T)[c][r].
+      f32x4 gkt = {0, 0, 0, 0}, gqt = {0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int lo = 32 * kb * kChunk + 4 * lane, hi = lo + 16 * kChunk;
+        const Frag8<bf16> fkt = cat8(lds_tr(tkt + lo), lds_tr(tkt + hi));
+        mfma_k32(gkt, fkt, cat8(lds_tr(tkh + lo), lds_tr(tkh + hi)));
+        mfma_k32(gqt, fkt, cat8(lds_tr(tqh + lo), lds_tr(tqh + hi)));
+      }
+      const float bn = sm.beta[x & 3][n];
+      f32x4 nn, aq;  // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * h + j;
+        nn[j] = n > r ? bn * gkt[j] : 0.0f;
+        aq[j] = n >= r ? gqt[j] : 0.0f;
+      }
+      lds_put(&sm.n[x & 1][n][4 * h], nn);  // row-major N
+      lds_put(&sm.am[x % 5][n][4 * h], aq);  // row-major A
+    };
+
+    // -------------------------------------------------------------- solve(x): one wave
+    auto solve = [&](int x) {
+      const bf16* tn = &sm.n[x & 1][0][0];
+      const Frag4<bf16> fnt = f4(lds_b64(tn + n * kChunk + 4 * h));  // A layout of N
+      const Frag4<bf16> fnc = f4(lds_tr(tn + 4 * lane));             // C layout of N
+      f32x4 y;  // Y0 = I - N (C layout)
+      const f32x4 nc = bf16x4_to_f32(fnc.v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (4 * h + j == n ? 1.0f : 0.0f) - nc[j];
+      // The A layout of X is the C layout of X^T, so the pairs (N^p, (N^p)^T) feed each other.
+      f32x4 n2c = {0, 0, 0, 0}, n2t = {0, 0, 0, 0}, n4c = {0, 0, 0, 0}, n4t = {0, 0, 0, 0}, n8t = {0, 0, 0, 0};
+      mfma_k16(n2c, fnt, fnc);
+      mfma_k16(n2t, fnc, fnt);
+      mfma_k16(y, frag4<bf16>(n2t), frag4<bf16>(y));  // (I + N^2) Y0
+      mfma_k16(n4c, frag4<bf16>(n2t), frag4<bf16>(n2c));
+      mfma_k16(n4t, frag4<bf16>(n2c), frag4<bf16>(n2t));
+      mfma_k16(y, frag4<bf16>(n4t), frag4<bf16>(y));  // (I + N^4) Y1
+      mfma_k16(n8t, frag4<bf16>(n4c), frag4<bf16>(n4t));
+      mfma_k16(y, frag4<bf16>(n8t), frag4<bf16>(y));  // (I + N)^{-1} = (I + N^8) Y2
+      const f32x4 m = y * sm.beta[x & 3][n];          // M = (I + N)^{-1} Diag(beta), C layout
+      lds_put(&sm.mt[x & 1][n][4 * h], m);            // row-major M^T
+    };
+
+    auto step = [&](int i, const Staged& cur, Staged& nxt) {
+      load_chunk(i + 2, nxt);
+      if (i >= 1 && i - 1 < nchunks && g == (i & 3)) gram(i - 1);
+      if (i >= 2 && i - 2 < nchunks && g == ((i + 2) & 3)) solve(i - 2);
+      if (i < nchunks) {
+        if (i < nchunks - 1 || tail == kChunk)
+          gate(i, std::false_type());
+        else
+          gate(i, std::true_type());
+      }
+      stage_chunk(i + 1, cur);
+      block_sync();
+    };
+
+    Staged A, B;
+    load_chunk(0, B);
+    stage_chunk(0, B);
+    load_chunk(1, A);
+    block_sync();
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, A, B);
+      step(i + 1, B, A);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                 const float* initial_state, void* o, float* final_state, int B, int T, int H,
+                                 hipStream_t stream) {
+  const int units = B * H;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(chunk_fwd_bf16_kernel, dim3(units), dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k,
+                     (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T, H);
+  return hipGetLastError();
+}
+
+}  // namespace kda
