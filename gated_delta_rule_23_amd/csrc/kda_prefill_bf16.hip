@@ -45,6 +45,7 @@ namespace {
 constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 32 state columns each
 constexpr int kThreads = 64 * 2 * kChainWaves;  // plus one gate wave per SIMD
 constexpr int kPadRow = 144;  // staged input row: 128 channels + 16 pad (288 B: the 4 rows a 16-lane group reads hit distinct banks)
+constexpr int kORow = 136;     // O staging row: 128 columns + 8 pad (the four rows one 2-byte write covers hit distinct banks)
 constexpr float kGateLog2 = kGateFloor * kLog2e;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -66,8 +67,8 @@ struct Smem {
   alignas(16) bf16 mt[2][kChunk][kChunk];       // M^T, row-major: solve (x+2) -> prep (x+3)
   alignas(16) float gamma_c[5][4][4][8];        // Gamma_C[16 rt + 4 g + q] at [g][q][rt]: gate (x) -> chain (x+4)
   alignas(16) float beta[4][kChunk];            // staged at x-1 -> solve (x+2)
-  alignas(16) bf16 ost[kChainWaves][2][kChunk][kChunk];  // per chain wave and column tile: O, [column][token]
-  alignas(16) float prefix[kChainWaves][2][kChunk][4];    // per gate wave and channel tile: gate partial sums
+  alignas(16) bf16 ost[2][kChunk][kORow];      // O, token-major: chain (x) at x+4 -> stored at x+5
+  alignas(16) float prefix[kChainWaves][kChunk][4][2];    // per gate wave: gate partial sums [channel][token group][tile]
 };
 
 __device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     f32x4 u[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};  // U tiles of the chunk whose chain runs next
 
     // ------------------------------------------------------------ prep(x): W and U tiles
-    auto prep = [&](int x) {
+    auto prep = [&](int x, f32x4 (&u_out)[2]) {
       const Frag4<bf16> fm = f4(lds_tr(&sm.mt[x & 1][0][0] + 4 * lane));  // A layout of M
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         mfma_k16(wc, fm, fkh);
         mfma_k16(uc, fm, fv);
         lds_put(&sm.w[x & 1][0][0] + ch * kChunk + 4 * h, wc);  // channel-major W
-        u[ct] = uc;
+        u_out[ct] = uc;
       }
     };
 
@@ -238,23 +239,33 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         mfma_k16(da, fa, fv);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[ct][rt], fkb[rt], fv);
-        // O = Qh S + A Vt, through this wave's LDS tile to token-major rows
-        bf16* ot = &sm.ost[c][ct][0][0];
-        lds_put(ot + n * kChunk + 4 * h, pq[ct] + da);
-        wave_lds_sync();
-        const bf16x4 orow = lds_tr(ot + 4 * lane);  // token l%16, columns 32c + 16ct + 4h .. +3
-        const rsrc_t ro = make_rsrc(o_seq + x * rows_step, rows_bytes(x));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, orow), ro,
-                                              n * tok_bytes + (32 * c + 16 * ct + 4 * h) * (int)sizeof(bf16), 0, 0);
+        // O = Qh S + A Vt into the token-major tile; stored from there next iteration
+        const f32x4 ov = pq[ct] + da;
+        bf16* ot = &sm.ost[x & 1][4 * h][32 * c + 16 * ct + n];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ot[j * kORow] = (bf16)ov[j];
       }
+    };
+    // O of chunk x from the LDS tile to o: chain wave c stores tokens 4c .. 4c+3,
+    // 16 bytes a lane, so every store instruction writes whole 256-byte rows.
+    auto store_o = [&](int x) {
+      const rsrc_t ro = make_rsrc(o_seq + x * rows_step, rows_bytes(x));
+      const int tok = 4 * c + h;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.ost[x & 1][tok][8 * n]);
+      __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + 16 * n, 0, 0);
     };
 
     block_sync();  // inputs of chunk 0 staged
     for (int i = 0; i < nsteps; ++i) {
+      if (i >= 5 && i - 5 < nchunks) store_o(i - 5);
+      f32x4 u_next[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+      if (i >= 3 && i - 3 < nchunks) prep(i - 3, u_next);
       if (i >= 4 && i - 4 < nchunks) chain(i - 4);
-      if (i >= 3 && i - 3 < nchunks) prep(i - 3);
+      u[0] = u_next[0];
+      u[1] = u_next[1];
       block_sync();
     }
+    if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1);  // not reached inside the loop
 
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
@@ -292,35 +303,52 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     };
 
     // -------------------------------------------------------------- gate(x)
-    auto gate = [&](int x, auto ragged) {
+    // Lane (l%16, h) handles channels 32g + l%16 and 32g + 16 + l%16 (tiles
+    // cs = 0, 1), tokens 4h .. 4h+3.
+    struct GateIn {
+      bf16x4 q[2], k[2], a[2];
+    };
+    auto gate_read = [&](int x, GateIn& in) {
+      // Lane (l%16, h) addresses row 4h + (l%16)/4, elements 32g + 16cs + 4(l%4) ..;
+      // the transposing read returns channel 32g + 16cs + l%16, tokens 4h .. 4h+3.
+      const bf16* base = &sm.qka[x & 1][0][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * g + 4 * (n & 3);
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
-        const int ch = 32 * g + 16 * cs + n;  // this lane's channel; tokens 4h .. 4h+3
-        // Lane (l%16, h) addresses row 4h + (l%16)/4, elements 32g + 16cs + 4(l%4) ..;
-        // the transposing read returns channel ch, tokens 4h .. 4h+3.
-        const bf16* in = &sm.qka[x & 1][0][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * g + 16 * cs + 4 * (n & 3);
-        const f32x4 qq = bf16x4_to_f32(lds_tr(in));
-        const f32x4 kk = bf16x4_to_f32(lds_tr(in + kChunk * kPadRow));
-        const f32x4 aa = bf16x4_to_f32(lds_tr(in + 2 * kChunk * kPadRow));
-        float b[4];
-        float run = 0.0f;
+        in.q[cs] = lds_tr(base + 16 * cs);
+        in.k[cs] = lds_tr(base + kChunk * kPadRow + 16 * cs);
+        in.a[cs] = lds_tr(base + 2 * kChunk * kPadRow + 16 * cs);
+      }
+    };
+    auto gate = [&](int x, const GateIn& in, auto ragged) {
+      float b[2][4], run[2];
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        const f32x4 aa = bf16x4_to_f32(in.a[cs]);
+        run[cs] = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float g2 = kGateLog2 * sigmoid_fast(aa[j]);
           if constexpr (decltype(ragged)::value) g2 = x * kChunk + 4 * h + j < T ? g2 : 0.0f;  // padded tokens: g = 0
-          run += g2;
-          b[j] = run;
+          run[cs] += g2;
+          b[cs][j] = run[cs];
         }
-        float* pre = &sm.prefix[g][cs][n][0];
-        pre[h] = run;
-        wave_lds_sync();
-        const f32x4 part = *reinterpret_cast<const f32x4*>(pre);
-        const float prefix = (h > 0 ? part[0] : 0.0f) + (h > 1 ? part[1] : 0.0f) + (h > 2 ? part[2] : 0.0f);
-        const float gam_c = __builtin_amdgcn_exp2f((part[0] + part[1]) + (part[2] + part[3]));
+      }
+      // prefix over the four token groups of each channel, through LDS
+      float* pre = &sm.prefix[g][n][0][0];
+      *reinterpret_cast<float2*>(pre + 2 * h) = make_float2(run[0], run[1]);
+      wave_lds_sync();
+      const f32x4 p01 = *reinterpret_cast<const f32x4*>(pre);      // groups 0, 1 of tiles 0, 1
+      const f32x4 p23 = *reinterpret_cast<const f32x4*>(pre + 4);  // groups 2, 3
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        const float t0 = p01[cs], t1 = p01[2 + cs], t2 = p23[cs], t3 = p23[2 + cs];
+        const float prefix = (h > 0 ? t0 : 0.0f) + (h > 1 ? t1 : 0.0f) + (h > 2 ? t2 : 0.0f);
+        const float gam_c = __builtin_amdgcn_exp2f((t0 + t1) + (t2 + t3));
+        const f32x4 kk = bf16x4_to_f32(in.k[cs]), qq = bf16x4_to_f32(in.q[cs]);
         f32x4 kh, qh, kt, kb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float b2 = b[j] + prefix;
+          const float b2 = b[cs][j] + prefix;
           const float gam = __builtin_amdgcn_exp2f(b2);
           const float inv = __builtin_amdgcn_exp2f(-b2);
           kh[j] = kk[j] * gam;
@@ -328,6 +356,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           kt[j] = kk[j] * inv;
           kb[j] = kt[j] * gam_c;
         }
+        const int ch = 32 * g + 16 * cs + n;
         const int cm = ch * kChunk + 4 * h;  // [channel][token] element offset
         lds_put(&sm.kh[x & 3][0][0] + cm, kh);
         lds_put(&sm.qh[x % 5][0][0] + cm, qh);
@@ -389,13 +418,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 
     auto step = [&](int i, const Staged& cur, Staged& nxt) {
       load_chunk(i + 2, nxt);
+      GateIn gin;
+      if (i < nchunks) gate_read(i, gin);  // issued first: the LDS latency hides under gram and solve
       if (i >= 1 && i - 1 < nchunks && g == (i & 3)) gram(i - 1);
       if (i >= 2 && i - 2 < nchunks && g == ((i + 2) & 3)) solve(i - 2);
       if (i < nchunks) {
         if (i < nchunks - 1 || tail == kChunk)
-          gate(i, std::false_type());
+          gate(i, gin, std::false_type());
         else
-          gate(i, std::true_type());
+          gate(i, gin, std::true_type());
       }
       stage_chunk(i + 1, cur);
       block_sync();
