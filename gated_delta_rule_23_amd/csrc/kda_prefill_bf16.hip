@@ -35,6 +35,10 @@
  * 16 elements read at byte 8 * lane thus arrives with lane i holding column
  * i, rows 4(l/16) .. +3 -- the accumulator (and B operand) layout -- while a
  * plain 8-byte read of row i, elements 4(l/16) .. +3 gives the A layout.
+ * Channel-major tiles keep a row's four 8-byte token groups in the order
+ * group ^ ((row / 4) % 4): with it the plain accesses of a wave (16 rows x 4
+ * groups) and the transposing reads (4 whole rows per 16 lanes) both spread
+ * over all LDS banks, where the unpermuted plain pattern costs 8x as long.
  */
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -52,23 +56,34 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-/* LDS rings.  A chunk x lives in slot x % (ring size) of each ring; the sizes
- * follow from the iteration that writes it and the last one that reads it. */
+/* LDS rings.  A chunk x lives in slot x % (ring size); the ring a buffer
+ * belongs to follows from the iteration that writes it and the last one that
+ * reads it.  Buffers of one ring share a slot, so one base address per ring
+ * and iteration serves all of them (the rest are immediate offsets). */
+struct Ring5 {
+  alignas(16) bf16 qh[kD][kChunk];          // channel-major [channel][token]: gate (x) -> gram (x+1), chain (x+4)
+  alignas(16) bf16 kb[kD][kChunk];          // gate (x) -> chain (x+4)
+  alignas(16) bf16 vin[kChunk][kPadRow];    // v, token-major: staged at x-1 -> prep (x+3)
+  alignas(16) bf16 am[kChunk][kChunk];      // A: gram (x+1) -> chain (x+4)
+  alignas(16) float gamma_c[4][4][8];       // Gamma_C[16 rt + 4 g + q] at [g][q][rt]: gate (x) -> chain (x+4)
+};
+struct Ring4 {
+  alignas(16) bf16 kh[kD][kChunk];          // gate (x) -> gram (x+1), prep (x+3)
+  alignas(16) float beta[kChunk];           // staged at x-1 -> solve (x+2)
+};
+struct Ring2 {
+  alignas(16) bf16 qka[3][kChunk][kPadRow];  // q, k, a, token-major: staged at x-1 -> gate (x)
+  alignas(16) bf16 kt[kD][kChunk];           // gate (x) -> gram (x+1)
+  alignas(16) bf16 w[kD][kChunk];            // prep (x+3) -> chain (x+4)
+  alignas(16) bf16 n[kChunk][kChunk];        // N: gram (x+1) -> solve (x+2)
+  alignas(16) bf16 mt[kChunk][kChunk];       // M^T: solve (x+2) -> prep (x+3)
+  alignas(16) bf16 ost[kChunk][kORow];       // O, token-major: chain (x) at x+4 -> stored at x+5
+};
 struct Smem {
-  alignas(16) bf16 qka[2][3][kChunk][kPadRow];  // q, k, a, token-major: staged at i-1, read by gate(i)
-  alignas(16) bf16 vin[5][kChunk][kPadRow];     // v, token-major: staged at x-1, read by prep(x) at x+3
-  alignas(16) bf16 kh[4][kD][kChunk];           // channel-major [channel][token]: gram (x+1), prep (x+3)
-  alignas(16) bf16 qh[5][kD][kChunk];           // gram (x+1), chain (x+4)
-  alignas(16) bf16 kt[2][kD][kChunk];           // gram (x+1)
-  alignas(16) bf16 kb[5][kD][kChunk];           // chain (x+4)
-  alignas(16) bf16 w[2][kD][kChunk];            // written by prep (x+3), read by chain (x+4)
-  alignas(16) bf16 n[2][kChunk][kChunk];        // N, row-major: gram (x+1) -> solve (x+2)
-  alignas(16) bf16 am[5][kChunk][kChunk];       // A, row-major: gram (x+1) -> chain (x+4)
-  alignas(16) bf16 mt[2][kChunk][kChunk];       // M^T, row-major: solve (x+2) -> prep (x+3)
-  alignas(16) float gamma_c[5][4][4][8];        // Gamma_C[16 rt + 4 g + q] at [g][q][rt]: gate (x) -> chain (x+4)
-  alignas(16) float beta[4][kChunk];            // staged at x-1 -> solve (x+2)
-  alignas(16) bf16 ost[2][kChunk][kORow];      // O, token-major: chain (x) at x+4 -> stored at x+5
-  alignas(16) float prefix[kChainWaves][kChunk][4][2];    // per gate wave: gate partial sums [channel][token group][tile]
+  Ring5 r5[5];
+  Ring4 r4[4];
+  Ring2 r2[2];
+  alignas(16) float prefix[kChainWaves][4][kChunk][2];  // per gate wave: gate partial sums [token group][channel][tile]
 };
 
 __device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
@@ -100,6 +115,7 @@ __device__ __forceinline__ float quad_bcast(float x) {
   constexpr int ctrl = J | (J << 2) | (J << 4) | (J << 6);
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, true));  // folds into the user
 }
+__device__ __forceinline__ void sm_prefix_put(float* p, float x, float y) { *reinterpret_cast<float2*>(p) = make_float2(x, y); }
 /* Orders LDS accesses of the lanes of one wave (a write, then reads of it by other lanes). */
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -149,6 +165,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   auto rows_bytes = [&](int x) { return (unsigned)x < (unsigned)nchunks ? (x == nchunks - 1 ? rows_tail : rows_full) : 0; };
   auto beta_bytes = [&](int x) { return (unsigned)x < (unsigned)nchunks ? (x == nchunks - 1 ? beta_tail : beta_full) : 0; };
 
+  // LDS element offsets inside a channel-major block of 16 rows x 16 tokens:
+  // the plain access of lane (l%16, h) (row l%16, tokens 4h ..) and the
+  // transposing read (rows 4h + (l%16)/4, tokens 4(l%4) ..), group-permuted.
+  const int pl_sw = n * kChunk + 4 * (h ^ (n >> 2));
+  const int tr_sw = (4 * h + (n >> 2)) * kChunk + 4 * ((n & 3) ^ h);
+
   if (wave < kChainWaves) {
     // ================================================================ chain wave c: columns 32c .. 32c+31
     const int c = wave;
@@ -170,44 +192,46 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           for (int j = 0; j < 4; ++j)
             sacc[ct][rt][j] = initial_state[((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + 32 * c + 16 * ct + n];
     }
-    f32x4 u[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};  // U tiles of the chunk whose chain runs next
+    // U tiles travel from prep (x) to chain (x) one iteration later in
+    // registers; two sets alternate between consecutive iterations.
+    f32x4 ua[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ub[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 
     // ------------------------------------------------------------ prep(x): W and U tiles
     auto prep = [&](int x, f32x4 (&u_out)[2]) {
-      const Frag4<bf16> fm = f4(lds_tr(&sm.mt[x & 1][0][0] + 4 * lane));  // A layout of M
+      const Frag4<bf16> fm = f4(lds_tr(&sm.r2[x & 1].mt[0][0] + tr_sw));  // A layout of M
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int ch = 32 * c + 16 * ct + n;
         // B layouts of Kh (channels 32c + 16ct ..) and of V (columns 32c + 16ct ..)
-        const Frag4<bf16> fkh = f4(lds_b64(&sm.kh[x & 3][0][0] + ch * kChunk + 4 * h));
+        const int blk = (32 * c + 16 * ct) * kChunk;  // rows 32c + 16ct ..
+        const Frag4<bf16> fkh = f4(lds_b64(&sm.r4[x & 3].kh[0][0] + blk + pl_sw));
         const Frag4<bf16> fv =
-            f4(lds_tr(&sm.vin[x % 5][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * c + 16 * ct + 4 * (n & 3)));
+            f4(lds_tr(&sm.r5[x % 5].vin[0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * c + 16 * ct + 4 * (n & 3)));
         f32x4 wc = {0, 0, 0, 0}, uc = {0, 0, 0, 0};
         mfma_k16(wc, fm, fkh);
         mfma_k16(uc, fm, fv);
-        lds_put(&sm.w[x & 1][0][0] + ch * kChunk + 4 * h, wc);  // channel-major W
+        lds_put(&sm.r2[x & 1].w[0][0] + blk + pl_sw, wc);  // channel-major W
         u_out[ct] = uc;
       }
     };
 
     // ------------------------------------------------------------ chain(x): the serial part
-    auto chain = [&](int x) {
-      const bf16* tw = &sm.w[x & 1][0][0];
-      const bf16* tq = &sm.qh[x % 5][0][0];
-      const bf16* tb = &sm.kb[x % 5][0][0];
+    auto chain = [&](int x, const f32x4 (&u)[2]) {
+      const bf16* tw = &sm.r2[x & 1].w[0][0];
+      const bf16* tq = &sm.r5[x % 5].qh[0][0];
+      const bf16* tb = &sm.r5[x % 5].kb[0][0];
       Frag8<bf16> fw[4], fq[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int lo = 32 * kb * kChunk + 4 * lane, hi = lo + 16 * kChunk;
+        const int lo = 32 * kb * kChunk + tr_sw, hi = lo + 16 * kChunk;
         fw[kb] = cat8(lds_tr(tw + lo), lds_tr(tw + hi));
         fq[kb] = cat8(lds_tr(tq + lo), lds_tr(tq + hi));
       }
-      const Frag4<bf16> fa = f4(lds_b64(&sm.am[x % 5][0][0] + n * kChunk + 4 * h));  // A layout of A
+      const Frag4<bf16> fa = f4(lds_b64(&sm.r5[x % 5].am[0][0] + pl_sw));  // A layout of A
       Frag4<bf16> fkb[8];
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt) fkb[rt] = f4(lds_b64(tb + (16 * rt + n) * kChunk + 4 * h));  // A layout of Kb^T
+      for (int rt = 0; rt < 8; ++rt) fkb[rt] = f4(lds_b64(tb + 16 * rt * kChunk + pl_sw));  // A layout of Kb^T
       // Gamma_C[16 rt + 4h + l%4] for all rt; row 16 rt + 4h + j comes from lane j of the quad
-      const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.gamma_c[x % 5][h][n & 3][0]);
+      const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.r5[x % 5].gamma_c[h][n & 3][0]);
       const f32x4 g_lo = gp[0], g_hi = gp[1];
       f32x4 pw[2], pq[2];
 #pragma unroll
@@ -227,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         // Diag(Gamma_C) S, under the MFMAs above
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-          const float g = rt < 4 ? g_lo[rt] : g_hi[rt - 4];
+          float g = rt < 4 ? g_lo[rt] : g_hi[rt - 4];
+          if (ct == 1) asm volatile("" : "+v"(g));  // a separate copy, so each broadcast folds into its multiply
           sacc[ct][rt][0] *= quad_bcast<0>(g);
           sacc[ct][rt][1] *= quad_bcast<1>(g);
           sacc[ct][rt][2] *= quad_bcast<2>(g);
@@ -240,10 +265,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[ct][rt], fkb[rt], fv);
         // O = Qh S + A Vt into the token-major tile; stored from there next iteration
-        const f32x4 ov = pq[ct] + da;
-        bf16* ot = &sm.ost[x & 1][4 * h][32 * c + 16 * ct + n];
+        const bf16x4 ob = __builtin_convertvector(pq[ct] + da, bf16x4);
+        bf16* ot = &sm.r2[x & 1].ost[4 * h][32 * c + 16 * ct + n];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ot[j * kORow] = (bf16)ov[j];
+        for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
       }
     };
     // O of chunk x from the LDS tile to o: chain wave c stores tokens 4c .. 4c+3,
@@ -251,19 +276,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     auto store_o = [&](int x) {
       const rsrc_t ro = make_rsrc(o_seq + x * rows_step, rows_bytes(x));
       const int tok = 4 * c + h;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.ost[x & 1][tok][8 * n]);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.r2[x & 1].ost[tok][8 * n]);
       __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + 16 * n, 0, 0);
     };
 
     block_sync();  // inputs of chunk 0 staged
-    for (int i = 0; i < nsteps; ++i) {
+    auto citer = [&](int i, const f32x4 (&u_use)[2], f32x4 (&u_make)[2]) {
       if (i >= 5 && i - 5 < nchunks) store_o(i - 5);
-      f32x4 u_next[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-      if (i >= 3 && i - 3 < nchunks) prep(i - 3, u_next);
-      if (i >= 4 && i - 4 < nchunks) chain(i - 4);
-      u[0] = u_next[0];
-      u[1] = u_next[1];
+      if (i >= 3 && i - 3 < nchunks) prep(i - 3, u_make);
+      if (i >= 4 && i - 4 < nchunks) chain(i - 4, u_use);
       block_sync();
+    };
+    for (int i = 0; i < nsteps; i += 2) {
+      citer(i, ua, ub);
+      citer(i + 1, ub, ua);
     }
     if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1);  // not reached inside the loop
 
@@ -296,10 +322,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       if (g == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, beta_bytes(x)), beta_off);
     };
     auto stage_chunk = [&](int x, const Staged& st) {
-      bf16* dst = g < 3 ? &sm.qka[x & 1][g][0][0] : &sm.vin[x % 5][0][0];
+      bf16* dst = g < 3 ? &sm.r2[x & 1].qka[g][0][0] : &sm.r5[x % 5].vin[0][0];
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + (4 * h + j) * kPadRow + 8 * n) = st.r[j];
-      if (g == 0 && h == 0) sm.beta[x & 3][n] = st.b;
+      if (g == 0 && h == 0) sm.r4[x & 3].beta[n] = st.b;
     };
 
     // -------------------------------------------------------------- gate(x)
@@ -311,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     auto gate_read = [&](int x, GateIn& in) {
       // Lane (l%16, h) addresses row 4h + (l%16)/4, elements 32g + 16cs + 4(l%4) ..;
       // the transposing read returns channel 32g + 16cs + l%16, tokens 4h .. 4h+3.
-      const bf16* base = &sm.qka[x & 1][0][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * g + 4 * (n & 3);
+      const bf16* base = &sm.r2[x & 1].qka[0][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * g + 4 * (n & 3);
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
         in.q[cs] = lds_tr(base + 16 * cs);
@@ -334,14 +360,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         }
       }
       // prefix over the four token groups of each channel, through LDS
-      float* pre = &sm.prefix[g][n][0][0];
-      *reinterpret_cast<float2*>(pre + 2 * h) = make_float2(run[0], run[1]);
+      const float2* pre = reinterpret_cast<const float2*>(&sm.prefix[g][0][n][0]);  // [group][channel] stride 16
+      sm_prefix_put(&sm.prefix[g][h][n][0], run[0], run[1]);
       wave_lds_sync();
-      const f32x4 p01 = *reinterpret_cast<const f32x4*>(pre);      // groups 0, 1 of tiles 0, 1
-      const f32x4 p23 = *reinterpret_cast<const f32x4*>(pre + 4);  // groups 2, 3
+      const float2 p0 = pre[0], p1 = pre[16], p2 = pre[32], p3 = pre[48];  // token groups 0 .. 3, tiles (x, y)
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
-        const float t0 = p01[cs], t1 = p01[2 + cs], t2 = p23[cs], t3 = p23[2 + cs];
+        const float t0 = cs ? p0.y : p0.x, t1 = cs ? p1.y : p1.x, t2 = cs ? p2.y : p2.x, t3 = cs ? p3.y : p3.x;
         const float prefix = (h > 0 ? t0 : 0.0f) + (h > 1 ? t1 : 0.0f) + (h > 2 ? t2 : 0.0f);
         const float gam_c = __builtin_amdgcn_exp2f((t0 + t1) + (t2 + t3));
         const f32x4 kk = bf16x4_to_f32(in.k[cs]), qq = bf16x4_to_f32(in.q[cs]);
@@ -356,32 +381,31 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           kt[j] = kk[j] * inv;
           kb[j] = kt[j] * gam_c;
         }
-        const int ch = 32 * g + 16 * cs + n;
-        const int cm = ch * kChunk + 4 * h;  // [channel][token] element offset
-        lds_put(&sm.kh[x & 3][0][0] + cm, kh);
-        lds_put(&sm.qh[x % 5][0][0] + cm, qh);
-        lds_put(&sm.kt[x & 1][0][0] + cm, kt);
-        lds_put(&sm.kb[x % 5][0][0] + cm, kb);
-        if (h == 0) sm.gamma_c[x % 5][n >> 2][n & 3][2 * g + cs] = gam_c;
+        const int cm = (32 * g + 16 * cs) * kChunk + pl_sw;  // channel ch, tokens 4h ..
+        lds_put(&sm.r4[x & 3].kh[0][0] + cm, kh);
+        lds_put(&sm.r5[x % 5].qh[0][0] + cm, qh);
+        lds_put(&sm.r2[x & 1].kt[0][0] + cm, kt);
+        lds_put(&sm.r5[x % 5].kb[0][0] + cm, kb);
+        if (h == 0) sm.r5[x % 5].gamma_c[n >> 2][n & 3][2 * g + cs] = gam_c;
       }
     };
 
     // -------------------------------------------------------------- gram(x): one wave
     auto gram = [&](int x) {
-      const bf16* tkt = &sm.kt[x & 1][0][0];
-      const bf16* tkh = &sm.kh[x & 3][0][0];
-      const bf16* tqh = &sm.qh[x % 5][0][0];
+      const bf16* tkt = &sm.r2[x & 1].kt[0][0];
+      const bf16* tkh = &sm.r4[x & 3].kh[0][0];
+      const bf16* tqh = &sm.r5[x % 5].qh[0][0];
       // C layouts: gkt = Kt Kh^T, lane (token c, h), register j <-> token r = 4h + j:
       // (Kh Kt^T)[c][r]; likewise gqt holds (Qh Kt^T)[c][r].
       f32x4 gkt = {0, 0, 0, 0}, gqt = {0, 0, 0, 0};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int lo = 32 * kb * kChunk + 4 * lane, hi = lo + 16 * kChunk;
+        const int lo = 32 * kb * kChunk + tr_sw, hi = lo + 16 * kChunk;
         const Frag8<bf16> fkt = cat8(lds_tr(tkt + lo), lds_tr(tkt + hi));
         mfma_k32(gkt, fkt, cat8(lds_tr(tkh + lo), lds_tr(tkh + hi)));
         mfma_k32(gqt, fkt, cat8(lds_tr(tqh + lo), lds_tr(tqh + hi)));
       }
-      const float bn = sm.beta[x & 3][n];
+      const float bn = sm.r4[x & 3].beta[n];
       f32x4 nn, aq;  // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -389,15 +413,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         nn[j] = n > r ? bn * gkt[j] : 0.0f;
         aq[j] = n >= r ? gqt[j] : 0.0f;
       }
-      lds_put(&sm.n[x & 1][n][4 * h], nn);  // row-major N
-      lds_put(&sm.am[x % 5][n][4 * h], aq);  // row-major A
+      lds_put(&sm.r2[x & 1].n[0][0] + pl_sw, nn);   // N, rows c
+      lds_put(&sm.r5[x % 5].am[0][0] + pl_sw, aq);  // A, rows c
     };
 
     // -------------------------------------------------------------- solve(x): one wave
     auto solve = [&](int x) {
-      const bf16* tn = &sm.n[x & 1][0][0];
-      const Frag4<bf16> fnt = f4(lds_b64(tn + n * kChunk + 4 * h));  // A layout of N
-      const Frag4<bf16> fnc = f4(lds_tr(tn + 4 * lane));             // C layout of N
+      const bf16* tn = &sm.r2[x & 1].n[0][0];
+      const Frag4<bf16> fnt = f4(lds_b64(tn + pl_sw));  // A layout of N
+      const Frag4<bf16> fnc = f4(lds_tr(tn + tr_sw));   // C layout of N
       f32x4 y;  // Y0 = I - N (C layout)
       const f32x4 nc = bf16x4_to_f32(fnc.v);
 #pragma unroll
@@ -412,8 +436,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       mfma_k16(y, frag4<bf16>(n4t), frag4<bf16>(y));  // (I + N^4) Y1
       mfma_k16(n8t, frag4<bf16>(n4c), frag4<bf16>(n4t));
       mfma_k16(y, frag4<bf16>(n8t), frag4<bf16>(y));  // (I + N)^{-1} = (I + N^8) Y2
-      const f32x4 m = y * sm.beta[x & 3][n];          // M = (I + N)^{-1} Diag(beta), C layout
-      lds_put(&sm.mt[x & 1][n][4 * h], m);            // row-major M^T
+      const f32x4 m = y * sm.r4[x & 3].beta[n];          // M = (I + N)^{-1} Diag(beta), C layout
+      lds_put(&sm.r2[x & 1].mt[0][0] + pl_sw, m);        // M^T, rows c
     };
 
     auto step = [&](int i, const Staged& cur, Staged& nxt) {
