@@ -38,7 +38,7 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "chunk_fwd_bf16_kernel"  # the kernel the bf16 prefill workload runs
 COPY_CALIBRATION_BYTES = 1 << 30  # one device-to-device copy of this many bytes (--calibrate-copy)
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
-                  for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_common.h", "kda_decode.hip")]
+                  for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_bf16_tiles.h", "kda_common.h", "kda_decode.hip")]
 
 
 def kernel_source_sha():

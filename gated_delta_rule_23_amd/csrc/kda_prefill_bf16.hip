@@ -40,6 +40,7 @@
  * groups) and the transposing reads (4 whole rows per 16 lanes) both spread
  * over all LDS banks, where the unpermuted plain pattern costs 8x as long.
  */
+#include "kda_bf16_tiles.h"
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -52,9 +53,6 @@ constexpr int kPadRow = 144;  // staged input row: 128 channels + 16 pad (288 B:
 constexpr int kORow = 136;     // O staging row: 128 columns + 8 pad (the four rows one 2-byte write covers hit distinct banks)
 constexpr float kGateLog2 = kGateFloor * kLog2e;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 /* LDS rings.  A chunk x lives in slot x % (ring size); the ring a buffer
  * belongs to follows from the iteration that writes it and the last one that
@@ -85,50 +83,6 @@ struct Smem {
   Ring2 r2[2];
   alignas(16) float prefix[kChainWaves][4][kChunk][2];  // per gate wave: gate partial sums [token group][channel][tile]
 };
-
-__device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
-}
-__device__ __forceinline__ bf16x4 lds_b64(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-__device__ __forceinline__ void lds_put(bf16* p, const f32x4& x) {
-  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(x, bf16x4);
-}
-__device__ __forceinline__ f32x4 bf16x4_to_f32(bf16x4 b) {
-  const u32x2 u = __builtin_bit_cast(u32x2, b);
-  f32x4 r = {__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
-             __uint_as_float(u[1] & 0xffff0000u)};
-  return r;
-}
-__device__ __forceinline__ Frag8<bf16> cat8(bf16x4 lo, bf16x4 hi) {
-  Frag8<bf16> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-__device__ __forceinline__ Frag4<bf16> f4(bf16x4 x) {
-  Frag4<bf16> f;
-  f.v = x;
-  return f;
-}
-/* The value of lane J of this lane's quad (DPP quad permutation). */
-template <int J>
-__device__ __forceinline__ float quad_bcast(float x) {
-  constexpr int ctrl = J | (J << 2) | (J << 4) | (J << 6);
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, true));  // folds into the user
-}
-__device__ __forceinline__ void sm_prefix_put(float* p, float x, float y) { *reinterpret_cast<float2*>(p) = make_float2(x, y); }
-/* Orders LDS accesses of the lanes of one wave (a write, then reads of it by other lanes). */
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-/* Workgroup barrier.  The chain and gate waves run separate loops, each with
- * exactly one of these per iteration and one before the loop. */
-__device__ __forceinline__ void block_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
@@ -170,6 +124,56 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   // transposing read (rows 4h + (l%16)/4, tokens 4(l%4) ..), group-permuted.
   const int pl_sw = n * kChunk + 4 * (h ^ (n >> 2));
   const int tr_sw = (4 * h + (n >> 2)) * kChunk + 4 * ((n & 3) ^ h);
+
+  // ---------------------------------------------------------------- gram(x): on one chain wave
+  auto gram = [&](int x) {
+    const bf16* tkt = &sm.r2[x & 1].kt[0][0];
+    const bf16* tkh = &sm.r4[x & 3].kh[0][0];
+    const bf16* tqh = &sm.r5[x % 5].qh[0][0];
+    // C layouts: gkt = Kt Kh^T, lane (token c, h), register j <-> token r = 4h + j:
+    // (Kh Kt^T)[c][r]; likewise gqt holds (Qh Kt^T)[c][r].
+    f32x4 gkt = {0, 0, 0, 0}, gqt = {0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int lo = 32 * kb * kChunk + tr_sw, hi = lo + 16 * kChunk;
+      const Frag8<bf16> fkt = cat8(lds_tr(tkt + lo), lds_tr(tkt + hi));
+      mfma_k32(gkt, fkt, cat8(lds_tr(tkh + lo), lds_tr(tkh + hi)));
+      mfma_k32(gqt, fkt, cat8(lds_tr(tqh + lo), lds_tr(tqh + hi)));
+    }
+    const float bn = sm.r4[x & 3].beta[n];
+    f32x4 nn, aq;  // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * h + j;
+      nn[j] = n > r ? bn * gkt[j] : 0.0f;
+      aq[j] = n >= r ? gqt[j] : 0.0f;
+    }
+    lds_put(&sm.r2[x & 1].n[0][0] + pl_sw, nn);   // N, rows c
+    lds_put(&sm.r5[x % 5].am[0][0] + pl_sw, aq);  // A, rows c
+  };
+
+  // ---------------------------------------------------------------- solve(x): on another
+  auto solve = [&](int x) {
+    const bf16* tn = &sm.r2[x & 1].n[0][0];
+    const Frag4<bf16> fnt = f4(lds_b64(tn + pl_sw));  // A layout of N
+    const Frag4<bf16> fnc = f4(lds_tr(tn + tr_sw));   // C layout of N
+    f32x4 y;  // Y0 = I - N (C layout)
+    const f32x4 nc = bf16x4_to_f32(fnc.v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = (4 * h + j == n ? 1.0f : 0.0f) - nc[j];
+    // The A layout of X is the C layout of X^T, so the pairs (N^p, (N^p)^T) feed each other.
+    f32x4 n2c = {0, 0, 0, 0}, n2t = {0, 0, 0, 0}, n4c = {0, 0, 0, 0}, n4t = {0, 0, 0, 0}, n8t = {0, 0, 0, 0};
+    mfma_k16(n2c, fnt, fnc);
+    mfma_k16(n2t, fnc, fnt);
+    mfma_k16(y, frag4<bf16>(n2t), frag4<bf16>(y));  // (I + N^2) Y0
+    mfma_k16(n4c, frag4<bf16>(n2t), frag4<bf16>(n2c));
+    mfma_k16(n4t, frag4<bf16>(n2c), frag4<bf16>(n2t));
+    mfma_k16(y, frag4<bf16>(n4t), frag4<bf16>(y));  // (I + N^4) Y1
+    mfma_k16(n8t, frag4<bf16>(n4c), frag4<bf16>(n4t));
+    mfma_k16(y, frag4<bf16>(n8t), frag4<bf16>(y));  // (I + N)^{-1} = (I + N^8) Y2
+    const f32x4 m = y * sm.r4[x & 3].beta[n];          // M = (I + N)^{-1} Diag(beta), C layout
+    lds_put(&sm.r2[x & 1].mt[0][0] + pl_sw, m);        // M^T, rows c
+  };
 
   if (wave < kChainWaves) {
     // ================================================================ chain wave c: columns 32c .. 32c+31
@@ -281,10 +285,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     };
 
     block_sync();  // inputs of chunk 0 staged
+    // Gram and solve ride on the chain waves (on two different SIMDs), whose
+    // serial step leaves room before the barrier.
     auto citer = [&](int i, const f32x4 (&u_use)[2], f32x4 (&u_make)[2]) {
       if (i >= 5 && i - 5 < nchunks) store_o(i - 5);
       if (i >= 3 && i - 3 < nchunks) prep(i - 3, u_make);
       if (i >= 4 && i - 4 < nchunks) chain(i - 4, u_use);
+      if (i >= 1 && i - 1 < nchunks && c == (i & 3)) gram(i - 1);
+      if (i >= 2 && i - 2 < nchunks && c == ((i + 2) & 3)) solve(i - 2);
       block_sync();
     };
     for (int i = 0; i < nsteps; i += 2) {
@@ -345,7 +353,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         in.a[cs] = lds_tr(base + 2 * kChunk * kPadRow + 16 * cs);
       }
     };
+    // 0/1 weights of token groups 0 .. 2 in this lane's exclusive prefix
+    const float wg0 = h > 0 ? 1.0f : 0.0f, wg1 = h > 1 ? 1.0f : 0.0f, wg2 = h > 2 ? 1.0f : 0.0f;
     auto gate = [&](int x, const GateIn& in, auto ragged) {
+      // Sums are kept in units of sigmoid(a); g log2(e) = kGateLog2 sigmoid(a).
       float b[2][4], run[2];
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
@@ -353,9 +364,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         run[cs] = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float g2 = kGateLog2 * sigmoid_fast(aa[j]);
-          if constexpr (decltype(ragged)::value) g2 = x * kChunk + 4 * h + j < T ? g2 : 0.0f;  // padded tokens: g = 0
-          run[cs] += g2;
+          float sg = sigmoid_fast(aa[j]);
+          if constexpr (decltype(ragged)::value) sg = x * kChunk + 4 * h + j < T ? sg : 0.0f;  // padded tokens: g = 0
+          run[cs] += sg;
           b[cs][j] = run[cs];
         }
       }
@@ -367,13 +378,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
         const float t0 = cs ? p0.y : p0.x, t1 = cs ? p1.y : p1.x, t2 = cs ? p2.y : p2.x, t3 = cs ? p3.y : p3.x;
-        const float prefix = (h > 0 ? t0 : 0.0f) + (h > 1 ? t1 : 0.0f) + (h > 2 ? t2 : 0.0f);
-        const float gam_c = __builtin_amdgcn_exp2f((t0 + t1) + (t2 + t3));
+        const float prefix = kGateLog2 * fmaf(wg2, t2, fmaf(wg1, t1, wg0 * t0));
+        const float gam_c = __builtin_amdgcn_exp2f(kGateLog2 * ((t0 + t1) + (t2 + t3)));
         const f32x4 kk = bf16x4_to_f32(in.k[cs]), qq = bf16x4_to_f32(in.q[cs]);
         f32x4 kh, qh, kt, kb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float b2 = b[cs][j] + prefix;
+          const float b2 = fmaf(kGateLog2, b[cs][j], prefix);
           const float gam = __builtin_amdgcn_exp2f(b2);
           const float inv = __builtin_amdgcn_exp2f(-b2);
           kh[j] = kk[j] * gam;
@@ -390,69 +401,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
     };
 
-    // -------------------------------------------------------------- gram(x): one wave
-    auto gram = [&](int x) {
-      const bf16* tkt = &sm.r2[x & 1].kt[0][0];
-      const bf16* tkh = &sm.r4[x & 3].kh[0][0];
-      const bf16* tqh = &sm.r5[x % 5].qh[0][0];
-      // C layouts: gkt = Kt Kh^T, lane (token c, h), register j <-> token r = 4h + j:
-      // (Kh Kt^T)[c][r]; likewise gqt holds (Qh Kt^T)[c][r].
-      f32x4 gkt = {0, 0, 0, 0}, gqt = {0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int lo = 32 * kb * kChunk + tr_sw, hi = lo + 16 * kChunk;
-        const Frag8<bf16> fkt = cat8(lds_tr(tkt + lo), lds_tr(tkt + hi));
-        mfma_k32(gkt, fkt, cat8(lds_tr(tkh + lo), lds_tr(tkh + hi)));
-        mfma_k32(gqt, fkt, cat8(lds_tr(tqh + lo), lds_tr(tqh + hi)));
-      }
-      const float bn = sm.r4[x & 3].beta[n];
-      f32x4 nn, aq;  // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * h + j;
-        nn[j] = n > r ? bn * gkt[j] : 0.0f;
-        aq[j] = n >= r ? gqt[j] : 0.0f;
-      }
-      lds_put(&sm.r2[x & 1].n[0][0] + pl_sw, nn);   // N, rows c
-      lds_put(&sm.r5[x % 5].am[0][0] + pl_sw, aq);  // A, rows c
-    };
-
-    // -------------------------------------------------------------- solve(x): one wave
-    auto solve = [&](int x) {
-      const bf16* tn = &sm.r2[x & 1].n[0][0];
-      const Frag4<bf16> fnt = f4(lds_b64(tn + pl_sw));  // A layout of N
-      const Frag4<bf16> fnc = f4(lds_tr(tn + tr_sw));   // C layout of N
-      f32x4 y;  // Y0 = I - N (C layout)
-      const f32x4 nc = bf16x4_to_f32(fnc.v);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = (4 * h + j == n ? 1.0f : 0.0f) - nc[j];
-      // The A layout of X is the C layout of X^T, so the pairs (N^p, (N^p)^T) feed each other.
-      f32x4 n2c = {0, 0, 0, 0}, n2t = {0, 0, 0, 0}, n4c = {0, 0, 0, 0}, n4t = {0, 0, 0, 0}, n8t = {0, 0, 0, 0};
-      mfma_k16(n2c, fnt, fnc);
-      mfma_k16(n2t, fnc, fnt);
-      mfma_k16(y, frag4<bf16>(n2t), frag4<bf16>(y));  // (I + N^2) Y0
-      mfma_k16(n4c, frag4<bf16>(n2t), frag4<bf16>(n2c));
-      mfma_k16(n4t, frag4<bf16>(n2c), frag4<bf16>(n2t));
-      mfma_k16(y, frag4<bf16>(n4t), frag4<bf16>(y));  // (I + N^4) Y1
-      mfma_k16(n8t, frag4<bf16>(n4c), frag4<bf16>(n4t));
-      mfma_k16(y, frag4<bf16>(n8t), frag4<bf16>(y));  // (I + N)^{-1} = (I + N^8) Y2
-      const f32x4 m = y * sm.r4[x & 3].beta[n];          // M = (I + N)^{-1} Diag(beta), C layout
-      lds_put(&sm.r2[x & 1].mt[0][0] + pl_sw, m);        // M^T, rows c
-    };
-
     auto step = [&](int i, const Staged& cur, Staged& nxt) {
+      stage_chunk(i + 1, cur);  // loaded one iteration ago
       load_chunk(i + 2, nxt);
       GateIn gin;
-      if (i < nchunks) gate_read(i, gin);  // issued first: the LDS latency hides under gram and solve
-      if (i >= 1 && i - 1 < nchunks && g == (i & 3)) gram(i - 1);
-      if (i >= 2 && i - 2 < nchunks && g == ((i + 2) & 3)) solve(i - 2);
+      if (i < nchunks) gate_read(i, gin);
       if (i < nchunks) {
         if (i < nchunks - 1 || tail == kChunk)
           gate(i, gin, std::false_type());
         else
           gate(i, gin, std::true_type());
       }
-      stage_chunk(i + 1, cur);
       block_sync();
     };
 
