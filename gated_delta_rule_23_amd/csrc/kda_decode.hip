@@ -14,7 +14,8 @@
  * 256-thread workgroup owns one (b, h) state and keeps it in registers
  * between the read and the write: thread t holds the float4 columns
  * 4 (t % 32) .. +3 of rows t / 32 + 8 m, m = 0..15, so every wave reads and
- * writes two whole 512-byte rows per instruction.
+ * writes two whole 512-byte rows per instruction.  State loads and stores
+ * carry the non-temporal hint (the state streams through once per step).
  */
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO* __restrict__ q, c
   const int cg = t & 31, rg = t >> 5;
   f32x4 s[16];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg + 8 * m) * kD + 4 * cg);
+  for (int m = 0; m < 16; ++m)  // streamed: read once, not reused by this launch
+    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg + 8 * m) * kD + 4 * cg));
   __syncthreads();
 
   f32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO* __restrict__ q, c
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     int i = rg + 8 * m;
-    *reinterpret_cast<f32x4*>(S + (size_t)i * kD + 4 * cg) = s_alpha[i] * s[m] + s_k[i] * be;
+    __builtin_nontemporal_store(s_alpha[i] * s[m] + s_k[i] * be, reinterpret_cast<f32x4*>(S + (size_t)i * kD + 4 * cg));
   }
 }
 
