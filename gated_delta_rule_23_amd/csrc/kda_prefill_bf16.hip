@@ -11,12 +11,18 @@
  * Folding M into W and U before the state arrives leaves three MFMA rounds
  * on the serial path (W S and Qh S, then A Vt and the state update).
  *
- * Mapping: one 512-thread workgroup per (b, h), 8 waves, two per SIMD: wave
- * c < 4 (the chain wave of SIMD c) owns state columns 32c .. 32c+31 (sixteen
- * 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD g)
- * owns key channels 32g .. 32g+31 of the per-chunk work, so every SIMD pairs
- * the MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the
- * main loop does, separated by one workgroup barrier:
+ * Mapping: 512-thread workgroups, 8 waves, two per SIMD.  The columns of S
+ * (value channels) evolve independently given the per-chunk operands, so a
+ * (b, h) sequence is served by one workgroup owning all 128 state columns or,
+ * when the grid would leave more than half the CUs idle, by two owning 64
+ * each (kCT, the 16-column tiles per chain wave, is 2 or 1); the two then
+ * repeat the column-independent per-chunk work, which costs nothing on CUs
+ * that would be idle and halves the serial step each one runs.  Wave c < 4
+ * (the chain wave of SIMD c) owns kCT 16-column tiles of the state (8 kCT
+ * 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD g) owns
+ * key channels 32g .. 32g+31 of the per-chunk work, so every SIMD pairs the
+ * MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the main
+ * loop does, separated by one workgroup barrier:
  *   gate waves:  loads of chunk i+2 (gate wave g: tensor g of q, k, a, v,
  *                16-byte buffer loads of 256-byte rows), staged to LDS
  *                token-major one iteration later; gate(i): lane (channel,
@@ -40,6 +46,8 @@
  * groups) and the transposing reads (4 whole rows per 16 lanes) both spread
  * over all LDS banks, where the unpermuted plain pattern costs 8x as long.
  */
+#include <atomic>
+
 #include "kda_bf16_tiles.h"
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -47,7 +55,7 @@
 namespace kda {
 namespace {
 
-constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 32 state columns each
+constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 16 kCT state columns each
 constexpr int kThreads = 64 * 2 * kChainWaves;  // plus one gate wave per SIMD
 constexpr int kPadRow = 144;  // staged input row: 128 channels + 16 pad (288 B: the 4 rows a 16-lane group reads hit distinct banks)
 constexpr int kORow = 136;     // O staging row: 128 columns + 8 pad (the four rows one 2-byte write covers hit distinct banks)
@@ -84,15 +92,24 @@ struct Smem {
   alignas(16) float prefix[kChainWaves][4][kChunk][2];  // per gate wave: gate partial sums [token group][channel][tile]
 };
 
+template <int kCT>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
                                                                   const bf16* __restrict__ v,
                                                                   const bf16* __restrict__ a,
                                                                   const float* __restrict__ beta,
                                                                   const float* initial_state, bf16* __restrict__ o,
-                                                                  float* final_state, int T, int H) {
+                                                                  float* final_state, int T, int H, int units) {
+  static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
   __shared__ Smem sm;
-  const int unit = blockIdx.x;  // b * H + h
+  // kCT == 2: workgroup = unit (b * H + h).  kCT == 1: workgroups come in
+  // groups of 16, slots 0..7 taking column half 0 of units 8 grp .. 8 grp + 7
+  // and slots 8..15 half 1 of the same units; dispatch deals workgroups to
+  // the XCDs round robin, so both halves of a unit share an XCD and its L2
+  // (they load the same input rows).
+  const int unit = kCT == 2 ? (int)blockIdx.x : 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7);
+  const int half = kCT == 2 ? 0 : (int)((blockIdx.x >> 3) & 1);
+  if (unit >= units) return;  // whole workgroup, before any barrier
   const int bb = unit / H, hh = unit % H;
   // The wave index is uniform; saying so keeps everything derived from it
   // (buffer resources, branch conditions) in scalar registers.
@@ -176,50 +193,58 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   };
 
   if (wave < kChainWaves) {
-    // ================================================================ chain wave c: columns 32c .. 32c+31
+    // ================================================================ chain wave c: columns col0 .. col0 + 16 kCT - 1
     const int c = wave;
+    const int col0 = kCT == 2 ? 32 * c : 64 * half + 16 * c;
     const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
-    f32x4 sacc[2][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][32c + 16 ct + l%16]
+    f32x4 sacc[kCT][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][col0 + 16 ct + l%16]
     const bool has_s0 = initial_state != nullptr;  // one test, so the loads below issue back to back
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[ct][rt][j] = 0.0f;
     if (has_s0) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            sacc[ct][rt][j] = initial_state[((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + 32 * c + 16 * ct + n];
+            sacc[ct][rt][j] = initial_state[((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n];
     }
     // U tiles travel from prep (x) to chain (x) one iteration later in
     // registers; two sets alternate between consecutive iterations.
-    f32x4 ua[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ub[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    f32x4 ua[kCT], ub[kCT];
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) ua[ct] = ub[ct] = f32x4{0, 0, 0, 0};
 
     // ------------------------------------------------------------ prep(x): W and U tiles
-    auto prep = [&](int x, f32x4 (&u_out)[2]) {
+    // W = M Kh for key channels 32c .. 32c+31 (all 128 across the four waves,
+    // every workgroup needs all of W); U = M V for this wave's state columns.
+    auto prep = [&](int x, f32x4 (&u_out)[kCT]) {
       const Frag4<bf16> fm = f4(lds_tr(&sm.r2[x & 1].mt[0][0] + tr_sw));  // A layout of M
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        // B layouts of Kh (channels 32c + 16ct ..) and of V (columns 32c + 16ct ..)
         const int blk = (32 * c + 16 * ct) * kChunk;  // rows 32c + 16ct ..
-        const Frag4<bf16> fkh = f4(lds_b64(&sm.r4[x & 3].kh[0][0] + blk + pl_sw));
-        const Frag4<bf16> fv =
-            f4(lds_tr(&sm.r5[x % 5].vin[0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * c + 16 * ct + 4 * (n & 3)));
-        f32x4 wc = {0, 0, 0, 0}, uc = {0, 0, 0, 0};
+        const Frag4<bf16> fkh = f4(lds_b64(&sm.r4[x & 3].kh[0][0] + blk + pl_sw));  // B layout of Kh
+        f32x4 wc = {0, 0, 0, 0};
         mfma_k16(wc, fm, fkh);
-        mfma_k16(uc, fm, fv);
         lds_put(&sm.r2[x & 1].w[0][0] + blk + pl_sw, wc);  // channel-major W
+      }
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        const Frag4<bf16> fv =  // B layout of V, columns col0 + 16ct ..
+            f4(lds_tr(&sm.r5[x % 5].vin[0][0] + (4 * h + (n >> 2)) * kPadRow + col0 + 16 * ct + 4 * (n & 3)));
+        f32x4 uc = {0, 0, 0, 0};
+        mfma_k16(uc, fm, fv);
         u_out[ct] = uc;
       }
     };
 
     // ------------------------------------------------------------ chain(x): the serial part
-    auto chain = [&](int x, const f32x4 (&u)[2]) {
+    auto chain = [&](int x, const f32x4 (&u)[kCT]) {
       const bf16* tw = &sm.r2[x & 1].w[0][0];
       const bf16* tq = &sm.r5[x % 5].qh[0][0];
       const bf16* tb = &sm.r5[x % 5].kb[0][0];
@@ -237,9 +262,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       // Gamma_C[16 rt + 4h + l%4] for all rt; row 16 rt + 4h + j comes from lane j of the quad
       const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.r5[x % 5].gamma_c[h][n & 3][0]);
       const f32x4 g_lo = gp[0], g_hi = gp[1];
-      f32x4 pw[2], pq[2];
+      f32x4 pw[kCT], pq[kCT];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < kCT; ++ct) {
         Frag8<bf16> sf[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) sf[kb] = frag8<bf16>(sacc[ct][2 * kb], sacc[ct][2 * kb + 1]);
@@ -251,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         for (int kb = 0; kb < 4; ++kb) mfma_k32(pq[ct], fq[kb], sf[kb]);
       }
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < kCT; ++ct) {
         // Diag(Gamma_C) S, under the MFMAs above
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
@@ -270,24 +295,28 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[ct][rt], fkb[rt], fv);
         // O = Qh S + A Vt into the token-major tile; stored from there next iteration
         const bf16x4 ob = __builtin_convertvector(pq[ct] + da, bf16x4);
-        bf16* ot = &sm.r2[x & 1].ost[4 * h][32 * c + 16 * ct + n];
+        bf16* ot = &sm.r2[x & 1].ost[4 * h][col0 + 16 * ct + n];
 #pragma unroll
         for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
       }
     };
     // O of chunk x from the LDS tile to o: chain wave c stores tokens 4c .. 4c+3,
-    // 16 bytes a lane, so every store instruction writes whole 256-byte rows.
+    // 16 bytes a lane, so every store instruction writes whole rows (256 bytes;
+    // with two workgroups per sequence, this workgroup's 128-byte half).
     auto store_o = [&](int x) {
       const rsrc_t ro = make_rsrc(o_seq + x * rows_step, rows_bytes(x));
       const int tok = 4 * c + h;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.r2[x & 1].ost[tok][8 * n]);
-      __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + 16 * n, 0, 0);
+      if (kCT == 2 || n < 8) {
+        const int cb = kCT == 2 ? 16 * n : 128 * half + 16 * n;  // byte offset in the row
+        const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + cb);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + cb, 0, 0);
+      }
     };
 
     block_sync();  // inputs of chunk 0 staged
     // Gram and solve ride on the chain waves (on two different SIMDs), whose
     // serial step leaves room before the barrier.
-    auto citer = [&](int i, const f32x4 (&u_use)[2], f32x4 (&u_make)[2]) {
+    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT]) {
       if (i >= 5 && i - 5 < nchunks) store_o(i - 5);
       if (i >= 3 && i - 3 < nchunks) prep(i - 3, u_make);
       if (i >= 4 && i - 4 < nchunks) chain(i - 4, u_use);
@@ -302,12 +331,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1);  // not reached inside the loop
 
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const size_t idx = ((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + 32 * c + 16 * ct + n;
+          const size_t idx = ((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n;
           final_state[idx] = sacc[ct][rt][j];
         }
   } else {
@@ -427,6 +456,24 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   }
 }
 
+/* Compute units of the current device, looked up once per device. */
+hipError_t device_cu_count(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  err = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess && dev >= 0 && dev < 64) cache[dev].store(*cus, std::memory_order_relaxed);
+  return err;
+}
+
 }  // namespace
 
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
@@ -434,8 +481,19 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
                                  hipStream_t stream) {
   const int units = B * H;
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(chunk_fwd_bf16_kernel, dim3(units), dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T, H);
+  int cus = 0;
+  const hipError_t err = device_cu_count(&cus);
+  if (err != hipSuccess) return err;
+  const int64_t groups = ((int64_t)units + 7) / 8;
+  if (16 * groups <= cus) {  // two workgroups per sequence still fit on the device at once
+    hipLaunchKernelGGL(chunk_fwd_bf16_kernel<1>, dim3((unsigned)(16 * groups)), dim3(kThreads), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o,
+                       final_state, T, H, units);
+  } else {
+    hipLaunchKernelGGL(chunk_fwd_bf16_kernel<2>, dim3(units), dim3(kThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
+                       H, units);
+  }
   return hipGetLastError();
 }
 
