@@ -22,7 +22,7 @@ __device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
 }
 __device__ __forceinline__ bf16x4 lds_b64(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ void lds_put(bf16* p, const f32x4& x) {
-  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(x, bf16x4);
+  *reinterpret_cast<bf16x4*>(p) = pack_bf16x4(x);
 }
 __device__ __forceinline__ f32x4 bf16x4_to_f32(bf16x4 b) {
   const u32x2 u = __builtin_bit_cast(u32x2, b);

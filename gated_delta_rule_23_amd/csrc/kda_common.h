@@ -20,6 +20,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+/* Four floats to bf16 (round to nearest even) as two packed conversions.
+ * Converting the halves as 2-vectors, joined as 32-bit words, keeps the
+ * compiler on the packed instruction; a 4-vector taken straight from an MFMA
+ * result is otherwise converted one element at a time and re-packed with
+ * permutes. */
+__device__ __forceinline__ bf16x4 pack_bf16x4(const f32x4& x) {
+  const bf16x2 lo = __builtin_convertvector(__builtin_shufflevector(x, x, 0, 1), bf16x2);
+  const bf16x2 hi = __builtin_convertvector(__builtin_shufflevector(x, x, 2, 3), bf16x2);
+  typedef uint32_t pair_t __attribute__((ext_vector_type(2)));
+  const pair_t u = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  return __builtin_bit_cast(bf16x4, u);
+}
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
@@ -149,7 +164,7 @@ template <typename T>
 __device__ __forceinline__ Frag4<T> frag4(const f32x4& x) {
   if constexpr (sizeof(T) == 2) {
     Frag4<T> f;
-    f.v = __builtin_convertvector(x, bf16x4);  // two packed conversions
+    f.v = pack_bf16x4(x);
     return f;
   } else {
     return frag4<T>(x[0], x[1], x[2], x[3]);
@@ -160,7 +175,7 @@ template <typename T>
 __device__ __forceinline__ Frag8<T> frag8(const f32x4& lo, const f32x4& hi) {
   Frag8<T> f;
   if constexpr (sizeof(T) == 2) {
-    f.v = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4), 0, 1, 2,
+    f.v = __builtin_shufflevector(pack_bf16x4(lo), pack_bf16x4(hi), 0, 1, 2,
                                   3, 4, 5, 6, 7);
   } else {
 #pragma unroll

@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[ct][rt], fkb[rt], fv);
         // O = Qh S + A Vt into the token-major tile; stored from there next iteration
-        const bf16x4 ob = __builtin_convertvector(pq[ct] + da, bf16x4);
+        const bf16x4 ob = pack_bf16x4(pq[ct] + da);
         bf16* ot = &sm.r2[x & 1].ost[4 * h][col0 + 16 * ct + n];
 #pragma unroll
         for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
