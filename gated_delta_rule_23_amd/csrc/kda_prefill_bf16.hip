@@ -23,9 +23,9 @@
  * key channels 32g .. 32g+31 of the per-chunk work, so every SIMD pairs the
  * MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the main
  * loop does, separated by one workgroup barrier:
- *   gate waves:  loads of chunk i+2 (gate wave g: tensor g of q, k, a, v,
+ *   gate waves:  loads of chunk i+3 (gate wave g: tensor g of q, k, a, v,
  *                16-byte buffer loads of 256-byte rows), staged to LDS
- *                token-major one iteration later; gate(i): lane (channel,
+ *                token-major two iterations later; gate(i): lane (channel,
  *                tokens 4(l/16) .. +3): g, the cumulative sums and the four
  *                scaled operands, stored channel-major; gram(i-1) on one wave:
  *                Kt Kh^T and Kt Qh^T masked into N and A; solve(i-2) on
@@ -142,6 +142,34 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   const int pl_sw = n * kChunk + 4 * (h ^ (n >> 2));
   const int tr_sw = (4 * h + (n >> 2)) * kChunk + 4 * ((n & 3) ^ h);
 
+  // ---------------------------------------------------------------- inputs
+  // Loader wave w (the chain waves with two workgroups per sequence, whose
+  // serial step leaves room; else the gate waves) stages tensor w % 4 (q, k,
+  // a, v), rows 4h .. 4h+3, 16 bytes (channels 8(l%16) .. +7) each; loader 0
+  // also beta.
+  constexpr bool kLoadsOnChain = kCT == 1;
+  const int ldw = wave & 3;
+  const char* ld_seq = reinterpret_cast<const char*>((ldw == 0 ? q : ldw == 1 ? k : ldw == 2 ? a : v) + seq_off);
+  const int ld_off = 4 * h * tok_bytes + 16 * n;
+  const char* beta_seq = reinterpret_cast<const char*>(beta + (int64_t)bb * T * H + hh);
+  const int beta_off = n * H * (int)sizeof(float);
+  struct Staged {
+    u32x4 r[4];  // rows 4h .. 4h+3
+    float b;     // beta of token l%16 (loader 0)
+  };
+  auto load_chunk = [&](int x, Staged& st) {
+    const rsrc_t r = make_rsrc(ld_seq + x * rows_step, rows_bytes(x));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off + j * tok_bytes, 0, 0);
+    if (ldw == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, beta_bytes(x)), beta_off);
+  };
+  auto stage_chunk = [&](int x, const Staged& st) {
+    bf16* dst = ldw < 3 ? &sm.r2[x & 1].qka[ldw][0][0] : &sm.r5[x % 5].vin[0][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + (4 * h + j) * kPadRow + 8 * n) = st.r[j];
+    if (ldw == 0 && h == 0) sm.r4[x & 3].beta[n] = st.b;
+  };
+
   // ---------------------------------------------------------------- gram(x): on one chain wave
   auto gram = [&](int x) {
     const bf16* tkt = &sm.r2[x & 1].kt[0][0];
@@ -213,6 +241,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             sacc[ct][rt][j] = initial_state[((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n];
+      // waited for here: left to their first use, inside the loop, the
+      // waits would be repeated every iteration
+      wait_vmem_all();
     }
     // U tiles travel from prep (x) to chain (x) one iteration later in
     // registers; two sets alternate between consecutive iterations.
@@ -303,8 +334,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     // O of chunk x from the LDS tile to o: chain wave c stores tokens 4c .. 4c+3,
     // 16 bytes a lane, so every store instruction writes whole rows (256 bytes;
     // with two workgroups per sequence, this workgroup's 128-byte half).
-    auto store_o = [&](int x) {
-      const rsrc_t ro = make_rsrc(o_seq + x * rows_step, rows_bytes(x));
+    auto store_o = [&](int x, auto all) {
+      const rsrc_t ro = make_rsrc(o_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
       const int tok = 4 * c + h;
       if (kCT == 2 || n < 8) {
         const int cb = kCT == 2 ? 16 * n : 128 * half + 16 * n;  // byte offset in the row
@@ -313,22 +344,38 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
     };
 
+    // With the loads here, chunk x is loaded at iteration x-2 into register
+    // set x % 2 and staged at the end of iteration x-1.
+    Staged la, lb;
+    if constexpr (kLoadsOnChain) {
+      load_chunk(0, la);
+      stage_chunk(0, la);
+      load_chunk(1, lb);
+    }
     block_sync();  // inputs of chunk 0 staged
     // Gram and solve ride on the chain waves (on two different SIMDs), whose
     // serial step leaves room before the barrier.
-    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT]) {
-      if (i >= 5 && i - 5 < nchunks) store_o(i - 5);
-      if (i >= 3 && i - 3 < nchunks) prep(i - 3, u_make);
-      if (i >= 4 && i - 4 < nchunks) chain(i - 4, u_use);
-      if (i >= 1 && i - 1 < nchunks && c == (i & 3)) gram(i - 1);
-      if (i >= 2 && i - 2 < nchunks && c == ((i + 2) & 3)) solve(i - 2);
+    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], Staged& ld_now, const Staged& ld_old,
+                     auto all) __attribute__((always_inline)) {
+      if constexpr (kLoadsOnChain) load_chunk(i + 2, ld_now);
+      constexpr bool kAll = decltype(all)::value;
+      if (kAll || (i >= 5 && i - 5 < nchunks)) store_o(i - 5, all);
+      if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
+      if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && c == (i & 3)) gram(i - 1);
+      if ((kAll || (i >= 2 && i - 2 < nchunks)) && c == ((i + 2) & 3)) solve(i - 2);
+      if constexpr (kLoadsOnChain) stage_chunk(i + 1, ld_old);
       block_sync();
     };
-    for (int i = 0; i < nsteps; i += 2) {
-      citer(i, ua, ub);
-      citer(i + 1, ub, ua);
-    }
-    if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1);  // not reached inside the loop
+    auto step2 = [&](int i, auto all) __attribute__((always_inline)) {
+      citer(i, ua, ub, la, lb, all);
+      citer(i + 1, ub, ua, lb, la, all);
+    };
+    int i = 0;
+    for (; i < 6 && i < nsteps; i += 2) step2(i, std::false_type());
+    for (; i + 1 <= nchunks; i += 2) step2(i, std::true_type());
+    for (; i < nsteps; i += 2) step2(i, std::false_type());
+    if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1, std::false_type());  // not reached inside the loop
 
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct)
@@ -342,29 +389,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   } else {
     // ================================================================ gate wave g: key channels 32g .. 32g+31
     const int g = wave - kChainWaves;
-    // Loads: gate wave g stages tensor g (q, k, a, v), rows 4h .. 4h+3,
-    // 16 bytes (channels 8(l%16) .. +7) each; gate wave 0 also beta.
-    const char* ld_seq = reinterpret_cast<const char*>((g == 0 ? q : g == 1 ? k : g == 2 ? a : v) + seq_off);
-    const int ld_off = 4 * h * tok_bytes + 16 * n;
-    const char* beta_seq = reinterpret_cast<const char*>(beta + (int64_t)bb * T * H + hh);
-    const int beta_off = n * H * (int)sizeof(float);
-    struct Staged {
-      u32x4 r[4];  // rows 4h .. 4h+3
-      float b;     // beta of token l%16 (gate wave 0)
-    };
-    auto load_chunk = [&](int x, Staged& st) {
-      const rsrc_t r = make_rsrc(ld_seq + x * rows_step, rows_bytes(x));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off + j * tok_bytes, 0, 0);
-      if (g == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, beta_bytes(x)), beta_off);
-    };
-    auto stage_chunk = [&](int x, const Staged& st) {
-      bf16* dst = g < 3 ? &sm.r2[x & 1].qka[g][0][0] : &sm.r5[x % 5].vin[0][0];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + (4 * h + j) * kPadRow + 8 * n) = st.r[j];
-      if (g == 0 && h == 0) sm.r4[x & 3].beta[n] = st.b;
-    };
-
     // -------------------------------------------------------------- gate(x)
     // Lane (l%16, h) handles channels 32g + l%16 and 32g + 16 + l%16 (tiles
     // cs = 0, 1), tokens 4h .. 4h+3.
@@ -430,9 +454,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
     };
 
-    auto step = [&](int i, const Staged& cur, Staged& nxt) {
-      stage_chunk(i + 1, cur);  // loaded one iteration ago
-      load_chunk(i + 2, nxt);
+    // Chunk x is loaded at iteration x-3 into register set x % 3 and staged
+    // at x-1: two iterations cover the latency of the loads.
+    auto step = [&](int i, const Staged& st1, Staged& st3) {
+      if constexpr (!kLoadsOnChain) {
+        stage_chunk(i + 1, st1);  // loaded two iterations ago
+        load_chunk(i + 3, st3);
+      }
       GateIn gin;
       if (i < nchunks) gate_read(i, gin);
       if (i < nchunks) {
@@ -444,15 +472,22 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       block_sync();
     };
 
-    Staged A, B;
-    load_chunk(0, B);
-    stage_chunk(0, B);
-    load_chunk(1, A);
-    block_sync();
-    for (int i = 0; i < nsteps; i += 2) {
-      step(i, A, B);
-      step(i + 1, B, A);
+    Staged A, B, C;  // chunks 0, 1, 2 (mod 3)
+    if constexpr (!kLoadsOnChain) {
+      load_chunk(0, A);
+      load_chunk(1, B);
+      load_chunk(2, C);
+      stage_chunk(0, A);
     }
+    block_sync();
+    int i = 0;
+    for (; i + 3 <= nsteps; i += 3) {
+      step(i, B, A);
+      step(i + 1, C, B);
+      step(i + 2, A, C);
+    }
+    if (i < nsteps) step(i, B, A);
+    if (i + 1 < nsteps) step(i + 1, C, B);
   }
 }
 
