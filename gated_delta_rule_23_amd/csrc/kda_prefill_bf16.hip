@@ -170,8 +170,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     if (ldw == 0 && h == 0) sm.r4[x & 3].beta[n] = st.b;
   };
 
-  // ---------------------------------------------------------------- gram(x): on one chain wave
-  auto gram = [&](int x) {
+  // ---------------------------------------------------------------- gram(x): N and A, on two chain waves
+  auto gram = [&](int x, auto want_n, auto want_a) {
+    constexpr bool kN = decltype(want_n)::value, kA = decltype(want_a)::value;
     const bf16* tkt = &sm.r2[x & 1].kt[0][0];
     const bf16* tkh = &sm.r4[x & 3].kh[0][0];
     const bf16* tqh = &sm.r5[x % 5].qh[0][0];
@@ -182,19 +183,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     for (int kb = 0; kb < 4; ++kb) {
       const int lo = 32 * kb * kChunk + tr_sw, hi = lo + 16 * kChunk;
       const Frag8<bf16> fkt = cat8(lds_tr(tkt + lo), lds_tr(tkt + hi));
-      mfma_k32(gkt, fkt, cat8(lds_tr(tkh + lo), lds_tr(tkh + hi)));
-      mfma_k32(gqt, fkt, cat8(lds_tr(tqh + lo), lds_tr(tqh + hi)));
+      if constexpr (kN) mfma_k32(gkt, fkt, cat8(lds_tr(tkh + lo), lds_tr(tkh + hi)));
+      if constexpr (kA) mfma_k32(gqt, fkt, cat8(lds_tr(tqh + lo), lds_tr(tqh + hi)));
     }
-    const float bn = sm.r4[x & 3].beta[n];
-    f32x4 nn, aq;  // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
+    // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
+    if constexpr (kN) {
+      const float bn = sm.r4[x & 3].beta[n];
+      f32x4 nn;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * h + j;
-      nn[j] = n > r ? bn * gkt[j] : 0.0f;
-      aq[j] = n >= r ? gqt[j] : 0.0f;
+      for (int j = 0; j < 4; ++j) nn[j] = n > 4 * h + j ? bn * gkt[j] : 0.0f;
+      lds_put(&sm.r2[x & 1].n[0][0] + pl_sw, nn);  // N, rows c
     }
-    lds_put(&sm.r2[x & 1].n[0][0] + pl_sw, nn);   // N, rows c
-    lds_put(&sm.r5[x % 5].am[0][0] + pl_sw, aq);  // A, rows c
+    if constexpr (kA) {
+      f32x4 aq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) aq[j] = n >= 4 * h + j ? gqt[j] : 0.0f;
+      lds_put(&sm.r5[x % 5].am[0][0] + pl_sw, aq);  // A, rows c
+    }
   };
 
   // ---------------------------------------------------------------- solve(x): on another
@@ -353,8 +358,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       load_chunk(1, lb);
     }
     block_sync();  // inputs of chunk 0 staged
-    // Gram and solve ride on the chain waves (on two different SIMDs), whose
-    // serial step leaves room before the barrier.
+    // The two Gram products and the solve ride on the chain waves (three
+    // different SIMDs), whose serial step leaves room before the barrier.
     auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], Staged& ld_now, const Staged& ld_old,
                      auto all) __attribute__((always_inline)) {
       if constexpr (kLoadsOnChain) load_chunk(i + 2, ld_now);
@@ -362,7 +367,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       if (kAll || (i >= 5 && i - 5 < nchunks)) store_o(i - 5, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
       if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
-      if ((kAll || (i >= 1 && i - 1 < nchunks)) && c == (i & 3)) gram(i - 1);
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && c == (i & 3)) gram(i - 1, std::true_type(), std::false_type());
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && c == ((i + 1) & 3)) gram(i - 1, std::false_type(), std::true_type());
       if ((kAll || (i >= 2 && i - 2 < nchunks)) && c == ((i + 2) & 3)) solve(i - 2);
       if constexpr (kLoadsOnChain) stage_chunk(i + 1, ld_old);
       block_sync();
