@@ -46,15 +46,8 @@ __device__ __forceinline__ float quad_bcast(float x) {
   constexpr int ctrl = J | (J << 2) | (J << 4) | (J << 6);
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, true));  // folds into the user
 }
-__device__ __forceinline__ void sm_prefix_put(float* p, float x, float y) { *reinterpret_cast<float2*>(p) = make_float2(x, y); }
 /* s_waitcnt vmcnt(0), the other counters untouched (gfx9 encoding). */
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8)); }
-/* Orders LDS accesses of the lanes of one wave (a write, then reads of it by other lanes). */
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 /* Workgroup barrier (the same fences as __syncthreads).  Kernels whose waves
  * run separate loops call it the same number of times on every path. */
 __device__ __forceinline__ void block_sync() {

@@ -89,7 +89,6 @@ struct Smem {
   Ring5 r5[5];
   Ring4 r4[4];
   Ring2 r2[2];
-  alignas(16) float prefix[kChainWaves][4][kChunk][2];  // per gate wave: gate partial sums [token group][channel][tile]
 };
 
 template <int kCT>
@@ -413,7 +412,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
     };
     // 0/1 weights of token groups 0 .. 2 in this lane's exclusive prefix
-    const float wg0 = h > 0 ? 1.0f : 0.0f, wg1 = h > 1 ? 1.0f : 0.0f, wg2 = h > 2 ? 1.0f : 0.0f;
+    // 0/1 weights of the two exchanged partial sums in this lane's exclusive prefix
+    const float w_odd = (h & 1) ? 1.0f : 0.0f, w_hi = h >= 2 ? 1.0f : 0.0f;
     auto gate = [&](int x, const GateIn& in, auto ragged) {
       // Sums are kept in units of sigmoid(a); g log2(e) = kGateLog2 sigmoid(a).
       float b[2][4], run[2];
@@ -429,16 +429,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           b[cs][j] = run[cs];
         }
       }
-      // prefix over the four token groups of each channel, through LDS
-      const float2* pre = reinterpret_cast<const float2*>(&sm.prefix[g][0][n][0]);  // [group][channel] stride 16
-      sm_prefix_put(&sm.prefix[g][h][n][0], run[0], run[1]);
-      wave_lds_sync();
-      const float2 p0 = pre[0], p1 = pre[16], p2 = pre[32], p3 = pre[48];  // token groups 0 .. 3, tiles (x, y)
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
-        const float t0 = cs ? p0.y : p0.x, t1 = cs ? p1.y : p1.x, t2 = cs ? p2.y : p2.x, t3 = cs ? p3.y : p3.x;
-        const float prefix = kGateLog2 * fmaf(wg2, t2, fmaf(wg1, t1, wg0 * t0));
-        const float gam_c = __builtin_amdgcn_exp2f(kGateLog2 * ((t0 + t1) + (t2 + t3)));
+        // Prefix over the four token groups (16-lane rows) of each channel, by
+        // row swaps in registers: e = r of rows (0, 0, 2, 2), o = of rows
+        // (1, 1, 3, 3); their sums s, swapped across the halves, give z = s of
+        // rows 0-1 and the other half's.
+        const auto eo = __builtin_amdgcn_permlane16_swap(__float_as_uint(run[cs]), __float_as_uint(run[cs]), false, false);
+        const float e = __uint_as_float(eo[0]), pair = e + __uint_as_float(eo[1]);
+        const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+        const float z_lo = __uint_as_float(zz[0]);  // r0 + r1 in every row
+        const float prefix = kGateLog2 * fmaf(w_hi, z_lo, w_odd * e);
+        const float gam_c = __builtin_amdgcn_exp2f(kGateLog2 * (z_lo + __uint_as_float(zz[1])));
         const f32x4 kk = bf16x4_to_f32(in.k[cs]), qq = bf16x4_to_f32(in.q[cs]);
         f32x4 kh, qh, kt, kb;
 #pragma unroll
