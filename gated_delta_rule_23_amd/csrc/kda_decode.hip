@@ -11,11 +11,14 @@
  *
  * The step is bound by HBM traffic: each state entry is read once and
  * written once (2 x 64 KiB per head), against 4 x 128 input values.  One
- * 256-thread workgroup owns one (b, h) state and keeps it in registers
+ * 1024-thread workgroup owns one (b, h) state and keeps it in registers
  * between the read and the write: thread t holds the float4 columns
- * 4 (t % 32) .. +3 of rows t / 32 + 8 m, m = 0..15, so every wave reads and
- * writes two whole 512-byte rows per instruction.  State loads and stores
- * carry the non-temporal hint (the state streams through once per step).
+ * 4 (t % 32) .. +3 of rows t / 32 + 32 m, m = 0..3, so every wave reads and
+ * writes two whole 512-byte rows per instruction.  (With the two barriers of
+ * the step in between, a state streams fastest in workgroups of 1024
+ * threads: measured on the same 1.6 GB with 256, 512 and 1024.)  State loads
+ * and stores carry the non-temporal hint (the state streams through once per
+ * step).
  */
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -28,13 +31,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+constexpr int kDecodeThreads = 1024;
+constexpr int kRowGroups = kDecodeThreads / 32;  // thread t: rows t / 32 + kRowGroups m
+constexpr int kRowsPerThread = kD / kRowGroups;
+
 template <typename IO>
-__global__ __launch_bounds__(256) void decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                                                      const IO* __restrict__ v, const IO* __restrict__ a,
                                                      const float* __restrict__ beta, float* __restrict__ state,
                                                      IO* __restrict__ o) {
   __shared__ float s_alpha[kD], s_ak[kD], s_aq[kD], s_k[kD], s_be[kD];
-  __shared__ f32x4 s_part[8][2][32];  // per row group: partial x and y, float4 per column group
+  __shared__ f32x4 s_part[kRowGroups / 2][2][32];  // per wave: partial x and y, float4 per column group
   __shared__ float s_dot[2];
 
   const int unit = blockIdx.x;  // b * H + h
@@ -54,28 +61,38 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO* __restrict__ q, c
   }
 
   const int cg = t & 31, rg = t >> 5;
-  f32x4 s[16];
+  f32x4 s[kRowsPerThread];
 #pragma unroll
-  for (int m = 0; m < 16; ++m)  // streamed: read once, not reused by this launch
-    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg + 8 * m) * kD + 4 * cg));
+  for (int m = 0; m < kRowsPerThread; ++m)  // streamed: read once, not reused by this launch
+    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg + kRowGroups * m) * kD + 4 * cg));
   __syncthreads();
 
   f32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    int i = rg + 8 * m;
+  for (int m = 0; m < kRowsPerThread; ++m) {
+    int i = rg + kRowGroups * m;
     x += s_ak[i] * s[m];
     y += s_aq[i] * s[m];
   }
-  s_part[rg][0][cg] = x;
-  s_part[rg][1][cg] = y;
+  // the two row groups of a wave (lanes 0..31 and 32..63, same columns) combined by a half swap
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto sx = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[j]), __float_as_uint(y[j]), false, false);
+    x[j] = __uint_as_float(sx[0]) + __uint_as_float(sx[1]);
+    y[j] = __uint_as_float(sy[0]) + __uint_as_float(sy[1]);
+  }
+  if ((t & 63) < 32) {
+    s_part[t >> 6][0][cg] = x;
+    s_part[t >> 6][1][cg] = y;
+  }
   __syncthreads();
 
   if (t < kD) {
     const float* px = reinterpret_cast<const float*>(&s_part[0][0][0]);
     float xs = 0.0f, ys = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < kRowGroups / 2; ++r) {
       xs += px[(r * 2 + 0) * kD + t];
       ys += px[(r * 2 + 1) * kD + t];
     }
@@ -88,8 +105,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO* __restrict__ q, c
 
   f32x4 be = *reinterpret_cast<const f32x4*>(&s_be[4 * cg]);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    int i = rg + 8 * m;
+  for (int m = 0; m < kRowsPerThread; ++m) {
+    int i = rg + kRowGroups * m;
     __builtin_nontemporal_store(s_alpha[i] * s[m] + s_k[i] * be, reinterpret_cast<f32x4*>(S + (size_t)i * kD + 4 * cg));
   }
 }
@@ -98,10 +115,10 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          void* o, int units, bool bf16_io, hipStream_t stream) {
   if (units == 0) return hipSuccess;
   if (bf16_io) {
-    hipLaunchKernelGGL(decode_kernel<bf16>, dim3(units), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+    hipLaunchKernelGGL(decode_kernel<bf16>, dim3(units), dim3(kDecodeThreads), 0, stream, (const bf16*)q, (const bf16*)k,
                        (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o);
   } else {
-    hipLaunchKernelGGL(decode_kernel<float>, dim3(units), dim3(256), 0, stream, (const float*)q, (const float*)k,
+    hipLaunchKernelGGL(decode_kernel<float>, dim3(units), dim3(kDecodeThreads), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)a, beta, state, (float*)o);
   }
   return hipGetLastError();
