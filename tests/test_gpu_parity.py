@@ -92,6 +92,26 @@ def test_small_and_ragged(kda, dtype, with_s0, shape):
     assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
 
 
+# The bf16 prefill serves a sequence with two workgroups (one per half of the
+# state columns) while 16 * ceil(units / 8) workgroups fit on the device, else
+# with one; these shapes straddle that limit on a 256-CU device (128 and 129
+# units) and give the one-workgroup layout a ragged tail and an initial state.
+LAYOUT_SHAPES = [(1, 128, 37), (1, 129, 37), (2, 65, 50)]
+
+
+@pytest.mark.parametrize("with_s0", [False, True])
+@pytest.mark.parametrize("shape", LAYOUT_SHAPES, ids=lambda s: "B%dH%dT%d" % s)
+def test_bf16_workgroup_layouts(kda, with_s0, shape):
+    B, H, T = shape
+    w = variant(WORKLOADS[2], index=52, dtype="bf16", s0_scale=0.5 if with_s0 else None)
+    print_case(f"case layout bf16 s0={with_s0} B={B} H={H} T={T}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, S = run_prefill(kda, x, x["s0"])
+    o_ref, S_ref = oracle_block(w, nb=B, nt=T, nh=H)
+    eo, es = rel_l2(to_np(o), o_ref), rel_l2(to_np(S), S_ref)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+
+
 def test_empty_sequence_copies_initial_state(kda):
     import torch
 
