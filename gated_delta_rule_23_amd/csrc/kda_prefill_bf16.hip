@@ -156,11 +156,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     u32x4 r[4];  // rows 4h .. 4h+3
     float b;     // beta of token l%16 (loader 0)
   };
-  auto load_chunk = [&](int x, Staged& st) {
-    const rsrc_t r = make_rsrc(ld_seq + x * rows_step, rows_bytes(x));
+  // full: chunk x is known to be whole (x < nchunks - 1), its resources need no range tests
+  auto load_chunk = [&](int x, Staged& st, auto full) {
+    constexpr bool kFull = decltype(full)::value;
+    const rsrc_t r = make_rsrc(ld_seq + x * rows_step, kFull ? rows_full : rows_bytes(x));
 #pragma unroll
     for (int j = 0; j < 4; ++j) st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off + j * tok_bytes, 0, 0);
-    if (ldw == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, beta_bytes(x)), beta_off);
+    if (ldw == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, kFull ? beta_full : beta_bytes(x)), beta_off);
   };
   auto stage_chunk = [&](int x, const Staged& st) {
     bf16* dst = ldw < 3 ? &sm.r2[x & 1].qka[ldw][0][0] : &sm.r5[x % 5].vin[0][0];
@@ -352,16 +354,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     // set x % 2 and staged at the end of iteration x-1.
     Staged la, lb;
     if constexpr (kLoadsOnChain) {
-      load_chunk(0, la);
+      load_chunk(0, la, std::false_type());
       stage_chunk(0, la);
-      load_chunk(1, lb);
+      load_chunk(1, lb, std::false_type());
     }
     block_sync();  // inputs of chunk 0 staged
     // The two Gram products and the solve ride on the chain waves (three
     // different SIMDs), whose serial step leaves room before the barrier.
     auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], Staged& ld_now, const Staged& ld_old,
                      auto all) __attribute__((always_inline)) {
-      if constexpr (kLoadsOnChain) load_chunk(i + 2, ld_now);
+      if constexpr (kLoadsOnChain) load_chunk(i + 2, ld_now, all);
       constexpr bool kAll = decltype(all)::value;
       if (kAll || (i >= 5 && i - 5 < nchunks)) store_o(i - 5, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
@@ -376,9 +378,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       citer(i, ua, ub, la, lb, all);
       citer(i + 1, ub, ua, lb, la, all);
     };
+    // Iterations 5 <= i <= nchunks - 4 have every section active and load a
+    // whole chunk (i + 2 < nchunks - 1): those run without range tests (pairs
+    // start at even i).
     int i = 0;
     for (; i < 6 && i < nsteps; i += 2) step2(i, std::false_type());
-    for (; i + 1 <= nchunks; i += 2) step2(i, std::true_type());
+    for (; i + 1 <= nchunks - 4; i += 2) step2(i, std::true_type());
     for (; i < nsteps; i += 2) step2(i, std::false_type());
     if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1, std::false_type());  // not reached inside the loop
 
@@ -411,7 +416,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         in.a[cs] = lds_tr(base + 2 * kChunk * kPadRow + 16 * cs);
       }
     };
-    // 0/1 weights of token groups 0 .. 2 in this lane's exclusive prefix
     // 0/1 weights of the two exchanged partial sums in this lane's exclusive prefix
     const float w_odd = (h & 1) ? 1.0f : 0.0f, w_hi = h >= 2 ? 1.0f : 0.0f;
     auto gate = [&](int x, const GateIn& in, auto ragged) {
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     auto step = [&](int i, const Staged& st1, Staged& st3) {
       if constexpr (!kLoadsOnChain) {
         stage_chunk(i + 1, st1);  // loaded two iterations ago
-        load_chunk(i + 3, st3);
+        load_chunk(i + 3, st3, std::false_type());
       }
       GateIn gin;
       if (i < nchunks) gate_read(i, gin);
@@ -482,9 +486,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 
     Staged A, B, C;  // chunks 0, 1, 2 (mod 3)
     if constexpr (!kLoadsOnChain) {
-      load_chunk(0, A);
-      load_chunk(1, B);
-      load_chunk(2, C);
+      load_chunk(0, A, std::false_type());
+      load_chunk(1, B, std::false_type());
+      load_chunk(2, C, std::false_type());
       stage_chunk(0, A);
     }
     block_sync();
