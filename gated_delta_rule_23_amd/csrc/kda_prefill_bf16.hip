@@ -503,11 +503,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   }
 }
 
-/* Compute units of the current device, looked up once per device. */
-hipError_t device_cu_count(int* cus) {
+/* Compute units of the device the stream runs on (the current device for the
+ * null stream), looked up once per device. */
+hipError_t device_cu_count(hipStream_t stream, int* cus) {
   static std::atomic<int> cache[64];
   int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev >= 0 && dev < 64) {
     const int c = cache[dev].load(std::memory_order_relaxed);
@@ -529,7 +530,7 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
   const int units = B * H;
   if (units == 0) return hipSuccess;
   int cus = 0;
-  const hipError_t err = device_cu_count(&cus);
+  const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
   const int64_t groups = ((int64_t)units + 7) / 8;
   if (16 * groups <= cus) {  // two workgroups per sequence still fit on the device at once
