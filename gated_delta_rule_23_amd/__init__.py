@@ -76,8 +76,10 @@ def _ptr(t):
 def _require(t, name, shape, dtype, device):
     if t is None:
         raise ValueError(f"{name} is required")
-    if not t.is_cuda or t.device != device:
-        raise ValueError(f"{name} must be on {device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (the device of q), got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -134,6 +136,7 @@ def kda_decode_step(q, k, v, a, beta, state, o=None, stream=None):
     B, H, Dk = q.shape
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
+    _require(q, "q", (B, H, Dk), dt, dev)
     _require(k, "k", (B, H, Dk), dt, dev)
     _require(a, "a", (B, H, Dk), dt, dev)
     if v.dim() != 3:

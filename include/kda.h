@@ -15,9 +15,10 @@
  *
  * Conventions for every entry point:
  *   - Every pointer is a device pointer (hipMalloc'd or equivalent), row-major,
- *     contiguous and 16-byte aligned.  The library allocates nothing, keeps no
- *     pointer after returning and holds no global state: it is re-entrant and
- *     thread-safe.
+ *     contiguous and 16-byte aligned.  The library allocates nothing and keeps
+ *     no pointer after returning.  Between calls it keeps only a per-device
+ *     cache of the compute-unit count and each thread's last error text, so
+ *     it is re-entrant and thread-safe.
  *   - Work is enqueued on `hip_stream` (NULL = the default stream) and runs
  *     asynchronously; the caller keeps every buffer alive until the stream has
  *     completed.  No entry point synchronises the host.

@@ -124,3 +124,42 @@ def test_last_error_is_per_thread(lib):
     th.join()
     assert seen["msg"] == ""
     assert "128" in kda.last_error()
+
+
+# --------------------------------------------------------------------------- Python binding checks (no launch)
+
+
+def _decode_args(torch, dtype):
+    B, H, D = 2, 3, 128
+    return dict(q=torch.zeros(B, H, D, dtype=dtype), k=torch.zeros(B, H, D, dtype=dtype),
+                v=torch.zeros(B, H, D, dtype=dtype), a=torch.zeros(B, H, D, dtype=dtype),
+                beta=torch.zeros(B, H), state=torch.zeros(B, H, D, D))
+
+
+def _chunk_args(torch, dtype):
+    B, T, H, D = 1, 5, 2, 128
+    return dict(q=torch.zeros(B, T, H, D, dtype=dtype), k=torch.zeros(B, T, H, D, dtype=dtype),
+                v=torch.zeros(B, T, H, D, dtype=dtype), a=torch.zeros(B, T, H, D, dtype=dtype),
+                beta=torch.zeros(B, T, H))
+
+
+@pytest.mark.parametrize("entry", ["decode", "chunk"])
+def test_binding_rejects_host_tensors_before_any_call(lib, entry):
+    """Host (CPU) tensors never reach the C ABI: their addresses are not
+    device pointers.  Every tensor argument is checked, q included."""
+    torch = pytest.importorskip("torch")
+    args = (_decode_args if entry == "decode" else _chunk_args)(torch, torch.float32)
+    fn = kda.kda_decode_step if entry == "decode" else kda.kda_chunk_fwd
+    with pytest.raises(ValueError, match="q must be a GPU tensor"):
+        fn(**args)
+
+
+def test_binding_rejects_wrong_shapes_and_dtypes(lib):
+    torch = pytest.importorskip("torch")
+    args = _decode_args(torch, torch.float32)
+    args["q"] = torch.zeros(2, 3, 64)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(**args)
+    args = _decode_args(torch, torch.float16)
+    with pytest.raises(TypeError, match="bfloat16 or float32"):
+        kda.kda_decode_step(**args)

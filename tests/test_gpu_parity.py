@@ -162,11 +162,17 @@ def test_chunk_split_invariance(kda, dtype, split):
         assert torch.equal(o_cat, o_full) and torch.equal(S2, S_full)
 
 
-def test_final_state_may_alias_initial_state(kda):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 3, 50), (2, 65, 50)], ids=lambda s: "B%dH%dT%d" % s)
+def test_final_state_may_alias_initial_state(kda, dtype, shape):
+    """In place (final_state is initial_state) equals out of place, bit for
+    bit, for both bf16 workgroup layouts (3 and 130 sequences) and fp32."""
     import torch
 
-    w = variant(WORKLOADS[2], index=54)
-    x = device_inputs(w, B=1, T=50, H=3)
+    B, H, T = shape
+    w = variant(WORKLOADS[2], index=54, dtype=dtype)
+    print_case(f"case alias {dtype} B={B} H={H} T={T}")
+    x = device_inputs(w, B=B, T=T, H=H)
     o_ref, S_ref = run_prefill(kda, x, x["s0"])
     state = x["s0"].clone()
     o, _ = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=state, final_state=state)
