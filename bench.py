@@ -41,11 +41,41 @@ KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
                   for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_bf16_tiles.h", "kda_common.h", "kda_decode.hip")]
 
 
+def strip_comments(text):
+    """C/C++ source with comments removed and every run of whitespace made one
+    space: what the compiler sees, up to formatting.  String and character
+    literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha():
+    """Hash of the kernel sources without their comments and formatting, so
+    that edits of comments keep the committed counter summary valid."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()[:16]
 
 

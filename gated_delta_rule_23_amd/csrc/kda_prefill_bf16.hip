@@ -14,26 +14,29 @@
  * Mapping: 512-thread workgroups, 8 waves, two per SIMD.  The columns of S
  * (value channels) evolve independently given the per-chunk operands, so a
  * (b, h) sequence is served by one workgroup owning all 128 state columns or,
- * when the grid would leave more than half the CUs idle, by two owning 64
- * each (kCT, the 16-column tiles per chain wave, is 2 or 1); the two then
- * repeat the column-independent per-chunk work, which costs nothing on CUs
- * that would be idle and halves the serial step each one runs.  Wave c < 4
- * (the chain wave of SIMD c) owns kCT 16-column tiles of the state (8 kCT
- * 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD g) owns
- * key channels 32g .. 32g+31 of the per-chunk work, so every SIMD pairs the
+ * while two workgroups per sequence still fit on the device at once, by two
+ * owning 64 each (kCT, the 16-column tiles per chain wave, is 2 or 1); the
+ * two then repeat the column-independent per-chunk work, which costs nothing
+ * on CUs that would be idle and halves the serial step each one runs.  Wave
+ * c < 4 (the chain wave of SIMD c) owns kCT 16-column tiles of the state
+ * (8 kCT 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD
+ * g) owns key channels 32g .. 32g+31 of the gate, so every SIMD pairs the
  * MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the main
  * loop does, separated by one workgroup barrier:
- *   gate waves:  loads of chunk i+3 (gate wave g: tensor g of q, k, a, v,
- *                16-byte buffer loads of 256-byte rows), staged to LDS
- *                token-major two iterations later; gate(i): lane (channel,
- *                tokens 4(l/16) .. +3): g, the cumulative sums and the four
- *                scaled operands, stored channel-major; gram(i-1) on one wave:
- *                Kt Kh^T and Kt Qh^T masked into N and A; solve(i-2) on
- *                another: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
- *                (N is nilpotent, the product is exact) and M;
- *   chain waves: prep(i-3): their tiles of W = M Kh and U = M V;
+ *   inputs:      chunk i+2 (chain waves, kCT = 1) or i+3 (gate waves, kCT =
+ *                2) loaded into registers, 16-byte buffer loads of 256-byte
+ *                rows, loader wave w taking tensor w % 4 of q, k, a, v; chunk
+ *                i+1 staged to LDS token-major;
+ *   gate waves:  gate(i): lane (channel, tokens 4(l/16) .. +3): g, the
+ *                cumulative sums and the four scaled operands, stored
+ *                channel-major;
+ *   chain waves: store_o(i-5); prep(i-3): their tiles of W = M Kh and U = M V;
  *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
- *                S <- Diag(Gamma_C) S + Kb^T Vt.
+ *                S <- Diag(Gamma_C) S + Kb^T Vt; then, on three of the four
+ *                in rotation, gram(i-1) as two products (Kt Kh^T masked into
+ *                N, Kt Qh^T into A) and solve(i-2): (I + N)^{-1} =
+ *                (I - N)(I + N^2)(I + N^4)(I + N^8) (N is nilpotent, the
+ *                product is exact) and M.
  * Operands change between token-major and channel-major through
  * ds_read_b64_tr_b16, which transposes 16-bit elements across the lanes of
  * each 16-lane group while it reads: lane i, element j of the result is
