@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "kda.h"
 #include "kda_internal.h"
 
@@ -53,6 +55,27 @@ kda_status check_ptr(const char* fn, const char* name, const void* p) {
   } while (0)
 
 }  // namespace
+
+namespace kda {
+
+hipError_t device_cu_count(hipStream_t stream, int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  err = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess && dev >= 0 && dev < 64) cache[dev].store(*cus, std::memory_order_relaxed);
+  return err;
+}
+
+}  // namespace kda
 
 extern "C" {
 

@@ -8,7 +8,11 @@
 
 namespace kda {
 
-/* units = B * H workgroups; q, k, v, a, o are [units, 128]; beta [units];
+/* Compute units of the device the stream runs on (the current device for the
+ * null stream), looked up once per device (kda_api.cpp). */
+hipError_t device_cu_count(hipStream_t stream, int* cus);
+
+/* units = B * H states; q, k, v, a, o are [units, 128]; beta [units];
  * state [units, 128, 128]. */
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
                          void* o, int units, bool bf16_io, hipStream_t stream);

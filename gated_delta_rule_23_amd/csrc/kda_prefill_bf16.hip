@@ -49,8 +49,6 @@
  * groups) and the transposing reads (4 whole rows per 16 lanes) both spread
  * over all LDS banks, where the unpermuted plain pattern costs 8x as long.
  */
-#include <atomic>
-
 #include "kda_bf16_tiles.h"
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -504,25 +502,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     if (i < nsteps) step(i, B, A);
     if (i + 1 < nsteps) step(i + 1, C, B);
   }
-}
-
-/* Compute units of the device the stream runs on (the current device for the
- * null stream), looked up once per device. */
-hipError_t device_cu_count(hipStream_t stream, int* cus) {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *cus = c;
-      return hipSuccess;
-    }
-  }
-  err = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (err == hipSuccess && dev >= 0 && dev < 64) cache[dev].store(*cus, std::memory_order_relaxed);
-  return err;
 }
 
 }  // namespace
