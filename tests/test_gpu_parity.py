@@ -320,6 +320,34 @@ def test_decode_agrees_with_prefill(kda, dtype):
     assert rel_l2(to_np(o_dec), to_np(o_pre)) <= tol and rel_l2(to_np(state), to_np(S_pre)) <= tol
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_grid_stride_ragged(kda, dtype):
+    """The decode grid strides over the states (four workgroups per compute
+    unit): 27 x 97 = 2619 states give 1024 workgroups on a 256-CU device, 571
+    of them three states and the rest two, so both register sets and both LDS
+    sets take turns and the last pass of a workgroup has nothing to prefetch.
+    Every state is checked on its own against the oracle."""
+    import torch
+
+    w = variant(WORKLOADS[4], index=72, dtype=dtype)
+    B, H, steps = 27, 97, 3
+    print_case(f"case decode grid stride {dtype} B={B} H={H} steps={steps}")
+    x, per_step = _decode_inputs(w, B, H, steps)
+    state = x["s0"].clone()
+    outs = [kda.kda_decode_step(s["q"], s["k"], s["v"], s["a"], s["beta"], state) for s in per_step]
+    torch.cuda.synchronize()
+    o = to_np(torch.stack(outs, dim=1))  # [B, steps, H, 128]
+    o_ref, S_ref = oracle_block(w, nb=B, nt=steps, nh=H)
+    S = to_np(state)
+    num_s = np.sqrt(((S - S_ref) ** 2).sum(axis=(2, 3)))
+    den_s = np.sqrt((S_ref ** 2).sum(axis=(2, 3)))
+    num_o = np.sqrt(((o - o_ref) ** 2).sum(axis=(1, 3)))
+    den_o = np.sqrt((o_ref ** 2).sum(axis=(1, 3)))
+    worst_s, worst_o = float((num_s / den_s).max()), float((num_o / den_o).max())
+    print_case(f"  worst per-state rel_l2 S={worst_s:.3e} o={worst_o:.3e}")
+    assert worst_s <= TOL[dtype] and worst_o <= TOL[dtype]
+
+
 def test_decode_empty_batch_is_a_no_op(kda):
     import torch
 
