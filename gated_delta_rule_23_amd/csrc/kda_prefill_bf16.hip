@@ -99,17 +99,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
                                                                   const bf16* __restrict__ a,
                                                                   const float* __restrict__ beta,
                                                                   const float* initial_state, bf16* __restrict__ o,
-                                                                  float* final_state, int T, int H, int units) {
+                                                                  float* final_state, int T, int H, int unit0,
+                                                                  int unit_end) {
   static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
   __shared__ Smem sm;
-  // kCT == 2: workgroup = unit (b * H + h).  kCT == 1: workgroups come in
-  // groups of 16, slots 0..7 taking column half 0 of units 8 grp .. 8 grp + 7
-  // and slots 8..15 half 1 of the same units; dispatch deals workgroups to
-  // the XCDs round robin, so both halves of a unit share an XCD and its L2
-  // (they load the same input rows).
-  const int unit = kCT == 2 ? (int)blockIdx.x : 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7);
+  // This launch serves units (b * H + h) unit0 .. unit_end - 1.  kCT == 2:
+  // workgroup i takes unit unit0 + i.  kCT == 1: workgroups come in groups of
+  // 16, slots 0..7 taking column half 0 of units 8 grp .. 8 grp + 7 (from
+  // unit0) and slots 8..15 half 1 of the same units; dispatch deals
+  // workgroups to the XCDs round robin, so both halves of a unit share an XCD
+  // and its L2 (they load the same input rows).
+  const int unit = unit0 + (kCT == 2 ? (int)blockIdx.x : 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7));
   const int half = kCT == 2 ? 0 : (int)((blockIdx.x >> 3) & 1);
-  if (unit >= units) return;  // whole workgroup, before any barrier
+  if (unit >= unit_end) return;  // whole workgroup, before any barrier
   const int bb = unit / H, hh = unit % H;
   // The wave index is uniform; saying so keeps everything derived from it
   // (buffer resources, branch conditions) in scalar registers.
@@ -514,15 +516,35 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
-  const int64_t groups = ((int64_t)units + 7) / 8;
-  if (16 * groups <= cus) {  // two workgroups per sequence still fit on the device at once
-    hipLaunchKernelGGL(chunk_fwd_bf16_kernel<1>, dim3((unsigned)(16 * groups)), dim3(kThreads), 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o,
-                       final_state, T, H, units);
+  auto launch = [&](bool pairs, int u0, int u1) {
+    if (pairs) {
+      const unsigned grid = (unsigned)(16 * (((int64_t)(u1 - u0) + 7) / 8));
+      hipLaunchKernelGGL(chunk_fwd_bf16_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
+                         H, u0, u1);
+    } else {
+      hipLaunchKernelGGL(chunk_fwd_bf16_kernel<2>, dim3((unsigned)(u1 - u0)), dim3(kThreads), 0, stream,
+                         (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state,
+                         (bf16*)o, final_state, T, H, u0, u1);
+    }
+  };
+  // Sequences that fit on the device at once as two workgroups each (one per
+  // compute unit, whole groups of 8).
+  const int pair_units = 8 * (cus / 16);
+  if (units <= pair_units) {
+    launch(true, 0, units);
+  } else if (units <= cus) {
+    launch(false, 0, units);  // one round of one workgroup per sequence
   } else {
-    hipLaunchKernelGGL(chunk_fwd_bf16_kernel<2>, dim3(units), dim3(kThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
-                       H, units);
+    // Several rounds of one workgroup per sequence; a partial last round
+    // that fits as pairs runs as pairs, in a launch of its own.
+    const int rest = units % cus;
+    if (rest != 0 && rest <= pair_units) {
+      launch(false, 0, units - rest);
+      launch(true, units - rest, units);
+    } else {
+      launch(false, 0, units);
+    }
   }
   return hipGetLastError();
 }

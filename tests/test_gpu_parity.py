@@ -94,9 +94,12 @@ def test_small_and_ragged(kda, dtype, with_s0, shape):
 
 # The bf16 prefill serves a sequence with two workgroups (one per half of the
 # state columns) while 16 * ceil(units / 8) workgroups fit on the device, else
-# with one; these shapes straddle that limit on a 256-CU device (128 and 129
-# units) and give the one-workgroup layout a ragged tail and an initial state.
-LAYOUT_SHAPES = [(1, 128, 37), (1, 129, 37), (2, 65, 50)]
+# with one; with more sequences than compute units, a partial last round that
+# fits as pairs runs as pairs in a second launch.  On a 256-CU device: 128
+# and 129 units straddle the first limit, 130 runs one round of single
+# workgroups, 300 runs 256 single workgroups and then 44 pairs, and 400 (144
+# left over, too many for pairs) runs single workgroups throughout.
+LAYOUT_SHAPES = [(1, 128, 37), (1, 129, 37), (2, 65, 50), (3, 100, 37), (4, 100, 20)]
 
 
 @pytest.mark.parametrize("with_s0", [False, True])
