@@ -28,6 +28,9 @@ kda_status fail(kda_status s, const char* fmt, ...) {
 kda_status ok() { return KDA_OK; }
 
 constexpr int kMaxPrefillHeads = 65536;
+// Sequences (B * H) per call: kernels form unit indices up to the count plus
+// one grid stride in 32-bit arithmetic, so the count keeps 2^20 of headroom.
+constexpr int64_t kMaxUnits = (1ll << 31) - (1ll << 20);
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -38,7 +41,9 @@ kda_status check_common(const char* fn, int B, int H, int Dk, int Dv, kda_dtype 
   if (Dk <= 0 || Dv <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: head sizes must be positive (Dk=%d, Dv=%d)", fn, Dk, Dv);
   if (Dk != 128 || Dv != 128)
     return fail(KDA_ERR_UNSUPPORTED, "%s: only Dk = Dv = 128 is implemented (got Dk=%d, Dv=%d)", fn, Dk, Dv);
-  if ((int64_t)B * H > 0x7FFFFFFFll) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H=%lld exceeds the grid limit", fn, (long long)B * H);
+  if ((int64_t)B * H > kMaxUnits)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H=%lld exceeds the limit of %lld sequences", fn, (long long)B * H,
+                (long long)kMaxUnits);
   return KDA_OK;
 }
 

@@ -42,8 +42,9 @@
  *                    return zero past T.
  *     One workgroup barrier per iteration separates producers and consumers
  *     of the four LDS stages.
- * Contractions take bf16 operands with fp32 accumulation for bf16 I/O, and
- * fp32 operands (16x16x4 fp32 MFMA) for fp32 I/O.  The state stays fp32.
+ * The kernel is written for an operand type OT and runs with OT = fp32 (fp32
+ * operands on the 16x16x4 fp32 MFMA, fp32 accumulation); the state stays
+ * fp32.
  */
 #include <type_traits>
 

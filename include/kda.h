@@ -30,6 +30,8 @@
  *     checked; beta is expected in [0, 1].
  *   - Only Dk = Dv = 128 is implemented (K3's head dimension); other positive
  *     sizes return KDA_ERR_UNSUPPORTED.
+ *   - B * H is at most 2^31 - 2^20; larger counts return
+ *     KDA_ERR_INVALID_ARGUMENT.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -102,6 +102,9 @@ def test_prefill_head_limit(lib):
 def test_size_overflow_is_rejected(lib):
     assert chunk(B=1 << 20, T=1 << 30, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT
     assert decode(B=1 << 20, H=1 << 20) == kda.KDA_ERR_INVALID_ARGUMENT
+    # B * H keeps 2^20 of headroom below 2^31 (unit index plus one grid stride)
+    assert decode(B=(1 << 31) - (1 << 20) + 1, H=1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "limit" in kda.last_error()
 
 
 def test_empty_batch_is_a_no_op(lib):
