@@ -32,9 +32,9 @@
  *                channel-major;
  *   chain waves: store_o(i-5); prep(i-3): their tiles of W = M Kh and U = M V;
  *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
- *                S <- Diag(Gamma_C) S + Kb^T Vt; then, on three of the four
- *                in rotation, gram(i-1) as two products (Kt Kh^T masked into
- *                N, Kt Qh^T into A) and solve(i-2): (I + N)^{-1} =
+ *                S <- Diag(Gamma_C) S + Kb^T Vt; then, on chain waves 1, 2
+ *                and 3, gram(i-1) as two products (Kt Kh^T masked into N,
+ *                Kt Qh^T into A) and solve(i-2): (I + N)^{-1} =
  *                (I - N)(I + N^2)(I + N^4)(I + N^8) (N is nilpotent, the
  *                product is exact) and M.
  * Operands change between token-major and channel-major through
@@ -49,6 +49,8 @@
  * groups) and the transposing reads (4 whole rows per 16 lanes) both spread
  * over all LDS banks, where the unpermuted plain pattern costs 8x as long.
  */
+#include <type_traits>
+
 #include "kda_bf16_tiles.h"
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -362,32 +364,50 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       load_chunk(1, lb, std::false_type());
     }
     block_sync();  // inputs of chunk 0 staged
-    // The two Gram products and the solve ride on the chain waves (three
-    // different SIMDs), whose serial step leaves room before the barrier.
+    // The two Gram products and the solve ride on chain waves 1, 2 and 3
+    // (three different SIMDs), whose serial step leaves room before the
+    // barrier; wave 0, which also loads beta, takes none.  Role: 0 Gram N,
+    // 1 Gram A, 2 solve, 3 none; kRole < 0 looks it up at run time.
     auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], Staged& ld_now, const Staged& ld_old,
-                     auto all) __attribute__((always_inline)) {
+                     auto all, auto role) __attribute__((always_inline)) {
       if constexpr (kLoadsOnChain) load_chunk(i + 2, ld_now, all);
       constexpr bool kAll = decltype(all)::value;
+      constexpr int kRole = decltype(role)::value;
+      constexpr int kRoleOf[kChainWaves] = {3, 0, 1, 2};
+      const int r = kRole >= 0 ? kRole : kRoleOf[c];
       if (kAll || (i >= 5 && i - 5 < nchunks)) store_o(i - 5, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
       if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
-      if ((kAll || (i >= 1 && i - 1 < nchunks)) && c == (i & 3)) gram(i - 1, std::true_type(), std::false_type());
-      if ((kAll || (i >= 1 && i - 1 < nchunks)) && c == ((i + 1) & 3)) gram(i - 1, std::false_type(), std::true_type());
-      if ((kAll || (i >= 2 && i - 2 < nchunks)) && c == ((i + 2) & 3)) solve(i - 2);
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 0) gram(i - 1, std::true_type(), std::false_type());
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1) gram(i - 1, std::false_type(), std::true_type());
+      if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 2) solve(i - 2);
       if constexpr (kLoadsOnChain) stage_chunk(i + 1, ld_old);
       block_sync();
     };
-    auto step2 = [&](int i, auto all) __attribute__((always_inline)) {
-      citer(i, ua, ub, la, lb, all);
-      citer(i + 1, ub, ua, lb, la, all);
+    auto step2 = [&](int i, auto all, auto role) __attribute__((always_inline)) {
+      citer(i, ua, ub, la, lb, all, role);
+      citer(i + 1, ub, ua, lb, la, all, role);
     };
+    using RunTimeRole = std::integral_constant<int, -1>;
     // Iterations 5 <= i <= nchunks - 4 have every section active and load a
     // whole chunk (i + 2 < nchunks - 1): those run without range tests (pairs
-    // start at even i).
+    // start at even i), in one copy of the loop per role, so that a wave's
+    // Gram or solve products share a basic block with its chain step and the
+    // compiler interleaves the two dependency chains.
     int i = 0;
-    for (; i < 6 && i < nsteps; i += 2) step2(i, std::false_type());
-    for (; i + 1 <= nchunks - 4; i += 2) step2(i, std::true_type());
-    for (; i < nsteps; i += 2) step2(i, std::false_type());
+    for (; i < 6 && i < nsteps; i += 2) step2(i, std::false_type(), RunTimeRole());
+    auto steady = [&](auto role) __attribute__((always_inline)) {
+      for (; i + 1 <= nchunks - 4; i += 2) step2(i, std::true_type(), role);
+    };
+    if (c == 1)
+      steady(std::integral_constant<int, 0>());
+    else if (c == 2)
+      steady(std::integral_constant<int, 1>());
+    else if (c == 3)
+      steady(std::integral_constant<int, 2>());
+    else
+      steady(std::integral_constant<int, 3>());
+    for (; i < nsteps; i += 2) step2(i, std::false_type(), RunTimeRole());
     if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1, std::false_type());  // not reached inside the loop
 
 #pragma unroll
