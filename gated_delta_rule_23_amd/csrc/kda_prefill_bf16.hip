@@ -30,7 +30,8 @@
  *   gate waves:  gate(i): lane (channel, tokens 4(l/16) .. +3): g, the
  *                cumulative sums and the four scaled operands, stored
  *                channel-major;
- *   chain waves: store_o(i-5); prep(i-3): their tiles of W = M Kh and U = M V;
+ *   chain waves: store_o(i-5) (chain wave 0 alone with kCT = 1); prep(i-3):
+ *                their tiles of W = M Kh and U = M V;
  *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
  *                S <- Diag(Gamma_C) S + Kb^T Vt; then, on chain waves 1, 2
  *                and 3, gram(i-1) as two products (Kt Kh^T masked into N,
@@ -342,16 +343,24 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
       }
     };
-    // O of chunk x from the LDS tile to o: chain wave c stores tokens 4c .. 4c+3,
-    // 16 bytes a lane, so every store instruction writes whole rows (256 bytes;
-    // with two workgroups per sequence, this workgroup's 128-byte half).
+    // O of chunk x from the LDS tile to o, 16 bytes a lane, every store
+    // instruction writing whole rows.  One state tile per chain wave: chain
+    // wave 0 (no Gram or solve) stores this workgroup's 128-byte half of all 16
+    // rows, lane (n, h) rows 2h + n/8 and 8 + 2h + n/8.  Two tiles: chain wave
+    // c stores rows 4c .. 4c+3.
     auto store_o = [&](int x, auto all) {
       const rsrc_t ro = make_rsrc(o_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
-      const int tok = 4 * c + h;
-      if (kCT == 2 || n < 8) {
-        const int cb = kCT == 2 ? 16 * n : 128 * half + 16 * n;  // byte offset in the row
+      auto store_row = [&](int tok, int cb) {
         const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + cb);
         __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + cb, 0, 0);
+      };
+      if constexpr (kCT == 1) {
+        if (c == 0) {
+          store_row(2 * h + (n >> 3), 128 * half + 16 * (n & 7));
+          store_row(8 + 2 * h + (n >> 3), 128 * half + 16 * (n & 7));
+        }
+      } else {
+        store_row(4 * c + h, 16 * n);
       }
     };
 
@@ -391,15 +400,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     using RunTimeRole = std::integral_constant<int, -1>;
     // Iterations 5 <= i <= nchunks - 4 have every section active and load a
     // whole chunk (i + 2 < nchunks - 1): those run without range tests (pairs
-    // start at even i), in one copy of the loop per role, so that a wave's
-    // Gram or solve products share a basic block with its chain step and the
-    // compiler interleaves the two dependency chains.
+    // start at even i).  With one state tile per chain wave they run in one
+    // copy of the loop per role, so that a wave's Gram or solve products share
+    // a basic block with its chain step and the compiler interleaves the two
+    // dependency chains; with two tiles the copies would spill registers.
     int i = 0;
     for (; i < 6 && i < nsteps; i += 2) step2(i, std::false_type(), RunTimeRole());
     auto steady = [&](auto role) __attribute__((always_inline)) {
       for (; i + 1 <= nchunks - 4; i += 2) step2(i, std::true_type(), role);
     };
-    if (c == 1)
+    if constexpr (kCT == 2)
+      steady(RunTimeRole());
+    else if (c == 1)
       steady(std::integral_constant<int, 0>());
     else if (c == 2)
       steady(std::integral_constant<int, 1>());
