@@ -23,10 +23,11 @@
  * g) owns key channels 32g .. 32g+31 of the gate, so every SIMD pairs the
  * MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the main
  * loop does, separated by one workgroup barrier:
- *   inputs:      chunk i+2 (chain waves, kCT = 1) or i+3 (gate waves, kCT =
- *                2) loaded into registers, 16-byte buffer loads of 256-byte
- *                rows, loader wave w taking tensor w % 4 of q, k, a, v; chunk
- *                i+1 staged to LDS token-major;
+ *   inputs:      beta, q, k, a of chunk i+2 and v of chunk i-1 loaded
+ *                straight into LDS token-major (buffer_load ... lds, 16 bytes
+ *                a lane, whole 256-byte rows), loader wave w (the chain waves
+ *                with kCT = 1, the gate waves with kCT = 2) taking tensor
+ *                w % 4 of q, k, a, v;
  *   gate waves:  gate(i): lane (channel, tokens 4(l/16) .. +3): g, the
  *                cumulative sums and the four scaled operands, stored
  *                channel-major;
@@ -61,7 +62,6 @@ namespace {
 
 constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 16 kCT state columns each
 constexpr int kThreads = 64 * 2 * kChainWaves;  // plus one gate wave per SIMD
-constexpr int kPadRow = 144;  // staged input row: 128 channels + 16 pad (288 B: the 4 rows a 16-lane group reads hit distinct banks)
 constexpr int kORow = 136;     // O staging row: 128 columns + 8 pad (the four rows one 2-byte write covers hit distinct banks)
 constexpr float kGateLog2 = kGateFloor * kLog2e;
 
@@ -73,16 +73,13 @@ constexpr float kGateLog2 = kGateFloor * kLog2e;
 struct Ring5 {
   alignas(16) bf16 qh[kD][kChunk];          // channel-major [channel][token]: gate (x) -> gram (x+1), chain (x+4)
   alignas(16) bf16 kb[kD][kChunk];          // gate (x) -> chain (x+4)
-  alignas(16) bf16 vin[kChunk][kPadRow];    // v, token-major: staged at x-1 -> prep (x+3)
   alignas(16) bf16 am[kChunk][kChunk];      // A: gram (x+1) -> chain (x+4)
   alignas(16) float gamma_c[4][4][8];       // Gamma_C[16 rt + 4 g + q] at [g][q][rt]: gate (x) -> chain (x+4)
 };
 struct Ring4 {
   alignas(16) bf16 kh[kD][kChunk];          // gate (x) -> gram (x+1), prep (x+3)
-  alignas(16) float beta[kChunk];           // staged at x-1 -> solve (x+2)
 };
 struct Ring2 {
-  alignas(16) bf16 qka[3][kChunk][kPadRow];  // q, k, a, token-major: staged at x-1 -> gate (x)
   alignas(16) bf16 kt[kD][kChunk];           // gate (x) -> gram (x+1)
   alignas(16) bf16 w[kD][kChunk];            // prep (x+3) -> chain (x+4)
   alignas(16) bf16 n[kChunk][kChunk];        // N: gram (x+1) -> solve (x+2)
@@ -94,6 +91,44 @@ struct Smem {
   Ring4 r4[4];
   Ring2 r2[2];
 };
+/* Inputs, written by the loads themselves (buffer_load ... lds: lane l's
+ * bytes land at the instruction's LDS base + 16 l, or + 4 l for beta).  A
+ * token-major row of 128 channels is therefore 256 bytes with no padding; its
+ * 16-byte slots sit XOR-permuted by in_swz(row) to keep the transposing reads
+ * of the gate and of prep free of bank conflicts. */
+struct InQKA {
+  alignas(16) bf16 t[3][kChunk][kD];  // q, k, a of chunk x (slot x % 3): loaded at x-2 -> gate (x)
+};
+struct InV {
+  alignas(16) bf16 t[kChunk][kD];  // v of chunk x (slot x % 3): loaded at x+1 -> prep (x+3)
+};
+struct InBeta {
+  alignas(16) float t[kChunk];  // beta of chunk x (slot x % 5): loaded at x-2 -> gram (x+1), solve (x+2)
+};
+
+/* 16-byte slot s of staged input row r is stored at slot s ^ in_swz(r): a
+ * 16-lane group of a transposing read touches rows 4h .. 4h+3 and two slots
+ * of each, which then cover 8 distinct slots; the two groups of a half wave
+ * (h even, h odd) fall 8 slots apart. */
+__device__ __forceinline__ int in_swz(int r) { return (2 * (r & 3)) ^ (8 * ((r >> 2) & 1)); }
+__device__ __forceinline__ int in_off(int r, int col) { return r * kD + 8 * ((col >> 3) ^ in_swz(r)) + (col & 7); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+/* 16 bytes per lane from the buffer at byte voff straight into LDS at
+ * lds_base + 16 lane (buffer_load_dwordx4 ... lds).  Written as inline
+ * assembly so that the compiler does not order every later LDS access of the
+ * wave behind it: the caller waits for these loads itself (vmcnt) before the
+ * workgroup barrier that publishes the data. */
+__device__ __forceinline__ void load_b128_to_lds(rsrc_t r, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+/* The same with 4 bytes per lane (lane l at lds_base + 4 l). */
+__device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 
 template <int kCT>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
@@ -106,6 +141,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
                                                                   int unit_end) {
   static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
   __shared__ Smem sm;
+  __shared__ InQKA s_qka[3];
+  __shared__ InV s_v[3];
+  __shared__ InBeta s_beta[5];
   // This launch serves units (b * H + h) unit0 .. unit_end - 1.  kCT == 2:
   // workgroup i takes unit unit0 + i.  kCT == 1: workgroups come in groups of
   // 16, slots 0..7 taking column half 0 of units 8 grp .. 8 grp + 7 (from
@@ -149,33 +187,45 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 
   // ---------------------------------------------------------------- inputs
   // Loader wave w (the chain waves with two workgroups per sequence, whose
-  // serial step leaves room; else the gate waves) stages tensor w % 4 (q, k,
-  // a, v), rows 4h .. 4h+3, 16 bytes (channels 8(l%16) .. +7) each; loader 0
-  // also beta.
+  // serial step leaves room; else the gate waves) loads tensor w % 4 (q, k,
+  // a, v) straight into LDS: in iteration i, q, k or a of chunk i+2 and v of
+  // chunk i-1 (needed only by prep, three iterations later), four
+  // instructions of four rows each; loader 0 also beta of chunk i+2.
   constexpr bool kLoadsOnChain = kCT == 1;
   const int ldw = wave & 3;
   const char* ld_seq = reinterpret_cast<const char*>((ldw == 0 ? q : ldw == 1 ? k : ldw == 2 ? a : v) + seq_off);
-  const int ld_off = 4 * h * tok_bytes + 16 * n;
   const char* beta_seq = reinterpret_cast<const char*>(beta + (int64_t)bb * T * H + hh);
   const int beta_off = n * H * (int)sizeof(float);
-  struct Staged {
-    u32x4 r[4];  // rows 4h .. 4h+3
-    float b;     // beta of token l%16 (loader 0)
-  };
-  // full: chunk x is known to be whole (x < nchunks - 1), its resources need no range tests
-  auto load_chunk = [&](int x, Staged& st, auto full) {
+  // full: the chunks are known to be whole, their resources need no range tests
+  auto dma_rows = [&](int x, bf16* dst, auto full) {
     constexpr bool kFull = decltype(full)::value;
     const rsrc_t r = make_rsrc(ld_seq + x * rows_step, kFull ? rows_full : rows_bytes(x));
+    // instruction j: rows 4j .. 4j+3, lane (n, h) row 4j + h, stored slot n
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.r[j] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off + j * tok_bytes, 0, 0);
-    if (ldw == 0) st.b = load_f32(make_rsrc(beta_seq + x * beta_step, kFull ? beta_full : beta_bytes(x)), beta_off);
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + h;
+      load_b128_to_lds(r, (uint32_t)(uintptr_t)(lds_void*)(dst + 4 * j * kD), row * tok_bytes + 16 * (n ^ in_swz(row)));
+    }
   };
-  auto stage_chunk = [&](int x, const Staged& st) {
-    bf16* dst = ldw < 3 ? &sm.r2[x & 1].qka[ldw][0][0] : &sm.r5[x % 5].vin[0][0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + (4 * h + j) * kPadRow + 8 * n) = st.r[j];
-    if (ldw == 0 && h == 0) sm.r4[x & 3].beta[n] = st.b;
+  // beta (loader 0, lanes 0..15: token l) and q, k or a (loaders 0..2) of chunk i+2
+  auto load_qka = [&](int i, auto full) {
+    constexpr bool kFull = decltype(full)::value;
+    if (ldw == 0 && lane < kChunk)
+      load_b32_to_lds(make_rsrc(beta_seq + (i + 2) * beta_step, kFull ? beta_full : beta_bytes(i + 2)),
+                      (uint32_t)(uintptr_t)(lds_void*)&s_beta[(i + 2) % 5].t[0], beta_off);
+    if (ldw < 3) dma_rows(i + 2, &s_qka[(i + 2) % 3].t[ldw][0][0], full);
   };
+  // v of chunk i-1 (loader 3), into the slot prep reads last at iteration i-1
+  auto load_v = [&](int i, auto full) {
+    if (ldw == 3) dma_rows(i - 1, &s_v[(i + 2) % 3].t[0][0], full);
+  };
+  auto load_inputs = [&](int i, auto full) {
+    load_qka(i, full);
+    load_v(i, full);
+  };
+  // Before the barrier that hands chunk operands on: every load but the
+  // last four issued (at least this iteration's rows) has landed.
+  auto wait_inputs = [&]() { __builtin_amdgcn_s_waitcnt(4 | (0x7 << 4) | (0xf << 8)); };
 
   // ---------------------------------------------------------------- gram(x): N and A, on two chain waves
   auto gram = [&](int x, auto want_n, auto want_a) {
@@ -195,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     }
     // N[c][r] = beta_c L[c][r] (c > r), A[c][r] (c >= r)
     if constexpr (kN) {
-      const float bn = sm.r4[x & 3].beta[n];
+      const float bn = s_beta[x % 5].t[n];
       f32x4 nn;
 #pragma unroll
       for (int j = 0; j < 4; ++j) nn[j] = n > 4 * h + j ? bn * gkt[j] : 0.0f;
@@ -228,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     mfma_k16(y, frag4<bf16>(n4t), frag4<bf16>(y));  // (I + N^4) Y1
     mfma_k16(n8t, frag4<bf16>(n4c), frag4<bf16>(n4t));
     mfma_k16(y, frag4<bf16>(n8t), frag4<bf16>(y));  // (I + N)^{-1} = (I + N^8) Y2
-    const f32x4 m = y * sm.r4[x & 3].beta[n];          // M = (I + N)^{-1} Diag(beta), C layout
+    const f32x4 m = y * s_beta[x % 5].t[n];            // M = (I + N)^{-1} Diag(beta), C layout
     lds_put(&sm.r2[x & 1].mt[0][0] + pl_sw, m);        // M^T, rows c
   };
 
@@ -279,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
         const Frag4<bf16> fv =  // B layout of V, columns col0 + 16ct ..
-            f4(lds_tr(&sm.r5[x % 5].vin[0][0] + (4 * h + (n >> 2)) * kPadRow + col0 + 16 * ct + 4 * (n & 3)));
+            f4(lds_tr(&s_v[x % 3].t[0][0] + in_off(4 * h + (n >> 2), col0 + 16 * ct + 4 * (n & 3))));
         f32x4 uc = {0, 0, 0, 0};
         mfma_k16(uc, fm, fv);
         u_out[ct] = uc;
@@ -364,38 +414,41 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
     };
 
-    // With the loads here, chunk x is loaded at iteration x-2 into register
-    // set x % 2 and staged at the end of iteration x-1.
-    Staged la, lb;
+    // With the loads here, beta, q, k and a of chunk x land during
+    // iteration x-2.
     if constexpr (kLoadsOnChain) {
-      load_chunk(0, la, std::false_type());
-      stage_chunk(0, la);
-      load_chunk(1, lb, std::false_type());
+      load_inputs(-2, std::false_type());
+      load_inputs(-1, std::false_type());
+      wait_inputs();
     }
-    block_sync();  // inputs of chunk 0 staged
+    block_sync();  // inputs of chunk 0 in LDS
     // The two Gram products and the solve ride on chain waves 1, 2 and 3
     // (three different SIMDs), whose serial step leaves room before the
     // barrier; wave 0, which also loads beta, takes none.  Role: 0 Gram N,
     // 1 Gram A, 2 solve, 3 none; kRole < 0 looks it up at run time.
-    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], Staged& ld_now, const Staged& ld_old,
-                     auto all, auto role) __attribute__((always_inline)) {
-      if constexpr (kLoadsOnChain) load_chunk(i + 2, ld_now, all);
+    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], auto all, auto role)
+                     __attribute__((always_inline)) {
       constexpr bool kAll = decltype(all)::value;
       constexpr int kRole = decltype(role)::value;
       constexpr int kRoleOf[kChainWaves] = {3, 0, 1, 2};
       const int r = kRole >= 0 ? kRole : kRoleOf[c];
+      // the stores go out before the input loads, which wait_inputs then leaves in flight
       if (kAll || (i >= 5 && i - 5 < nchunks)) store_o(i - 5, all);
+      if constexpr (kLoadsOnChain) load_qka(i, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
+      if constexpr (kLoadsOnChain) load_v(i, all);
       if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 0) gram(i - 1, std::true_type(), std::false_type());
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1) gram(i - 1, std::false_type(), std::true_type());
       if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 2) solve(i - 2);
-      if constexpr (kLoadsOnChain) stage_chunk(i + 1, ld_old);
+      if constexpr (kLoadsOnChain) {
+        wait_inputs();
+      }
       block_sync();
     };
     auto step2 = [&](int i, auto all, auto role) __attribute__((always_inline)) {
-      citer(i, ua, ub, la, lb, all, role);
-      citer(i + 1, ub, ua, lb, la, all, role);
+      citer(i, ua, ub, all, role);
+      citer(i + 1, ub, ua, all, role);
     };
     using RunTimeRole = std::integral_constant<int, -1>;
     // Iterations 5 <= i <= nchunks - 4 have every section active and load a
@@ -443,12 +496,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     auto gate_read = [&](int x, GateIn& in) {
       // Lane (l%16, h) addresses row 4h + (l%16)/4, elements 32g + 16cs + 4(l%4) ..;
       // the transposing read returns channel 32g + 16cs + l%16, tokens 4h .. 4h+3.
-      const bf16* base = &sm.r2[x & 1].qka[0][0][0] + (4 * h + (n >> 2)) * kPadRow + 32 * g + 4 * (n & 3);
+      const bf16* tile = &s_qka[x % 3].t[0][0][0];
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
-        in.q[cs] = lds_tr(base + 16 * cs);
-        in.k[cs] = lds_tr(base + kChunk * kPadRow + 16 * cs);
-        in.a[cs] = lds_tr(base + 2 * kChunk * kPadRow + 16 * cs);
+        const int off = in_off(4 * h + (n >> 2), 32 * g + 16 * cs + 4 * (n & 3));
+        in.q[cs] = lds_tr(tile + off);
+        in.k[cs] = lds_tr(tile + kChunk * kD + off);
+        in.a[cs] = lds_tr(tile + 2 * kChunk * kD + off);
       }
     };
     // 0/1 weights of the two exchanged partial sums in this lane's exclusive prefix
@@ -501,40 +555,31 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
     };
 
-    // Chunk x is loaded at iteration x-3 into register set x % 3 and staged
-    // at x-1: two iterations cover the latency of the loads.
-    auto step = [&](int i, const Staged& st1, Staged& st3) {
-      if constexpr (!kLoadsOnChain) {
-        stage_chunk(i + 1, st1);  // loaded two iterations ago
-        load_chunk(i + 3, st3, std::false_type());
-      }
+    // With the loads here, as on the chain waves with two workgroups per
+    // sequence: beta, q, k and a of chunk x land during iteration x-2.
+    auto step = [&](int i) {
       GateIn gin;
       if (i < nchunks) gate_read(i, gin);
+      if constexpr (!kLoadsOnChain) load_inputs(i, std::false_type());
       if (i < nchunks) {
         if (i < nchunks - 1 || tail == kChunk)
           gate(i, gin, std::false_type());
         else
           gate(i, gin, std::true_type());
       }
+      if constexpr (!kLoadsOnChain) {
+        wait_inputs();
+      }
       block_sync();
     };
 
-    Staged A, B, C;  // chunks 0, 1, 2 (mod 3)
     if constexpr (!kLoadsOnChain) {
-      load_chunk(0, A, std::false_type());
-      load_chunk(1, B, std::false_type());
-      load_chunk(2, C, std::false_type());
-      stage_chunk(0, A);
+      load_inputs(-2, std::false_type());
+      load_inputs(-1, std::false_type());
+      wait_inputs();
     }
     block_sync();
-    int i = 0;
-    for (; i + 3 <= nsteps; i += 3) {
-      step(i, B, A);
-      step(i + 1, C, B);
-      step(i + 2, A, C);
-    }
-    if (i < nsteps) step(i, B, A);
-    if (i + 1 < nsteps) step(i + 1, C, B);
+    for (int i = 0; i < nsteps; ++i) step(i);
   }
 }
 
