@@ -116,17 +116,20 @@ __device__ __forceinline__ int in_off(int r, int col) { return r * kD + 8 * ((co
 typedef __attribute__((address_space(3))) void lds_void;
 
 /* 16 bytes per lane from the buffer at byte voff straight into LDS at
- * lds_base + 16 lane (buffer_load_dwordx4 ... lds).  Written as inline
- * assembly so that the compiler does not order every later LDS access of the
- * wave behind it: the caller waits for these loads itself (vmcnt) before the
- * workgroup barrier that publishes the data. */
+ * lds_base + 16 lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base, and
+ * an instruction reading M0 needs one wait state after the scalar write).
+ * Written as inline assembly so that the compiler does not order every later
+ * LDS access of the wave behind it: the caller waits for these loads itself
+ * (vmcnt) before the workgroup barrier that publishes the data. */
 __device__ __forceinline__ void load_b128_to_lds(rsrc_t r, uint32_t lds_base, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff),
+               "s"(r)
                : "memory", "m0");
 }
 /* The same with 4 bytes per lane (lane l at lds_base + 4 l). */
 __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff),
+               "s"(r)
                : "memory", "m0");
 }
 
