@@ -358,3 +358,63 @@ def test_decode_empty_batch_is_a_no_op(kda):
     s = torch.empty((0, 4, 128, 128), dtype=torch.float32, device="cuda")
     o = kda.kda_decode_step(z, z, z, z, torch.empty((0, 4), device="cuda"), s)
     assert o.shape == (0, 4, 128)
+
+
+# --------------------------------------------------------------------------- streams and threads
+
+
+def test_user_stream_matches_default_stream(kda):
+    """Work goes to the stream passed in (torch's current stream by default):
+    prefill and decode on a side stream give the default stream's bits."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=56)
+    x = device_inputs(w, B=2, T=70, H=3)
+    o_ref, S_ref = run_prefill(kda, x, x["s0"])
+    state_ref = x["s0"].clone()
+    q1, k1, v1, a1 = (x[t][:, 0].contiguous() for t in ("q", "k", "v", "a"))
+    b1 = x["beta"][:, 0].contiguous()
+    od_ref = kda.kda_decode_step(q1, k1, v1, a1, b1, state_ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o, S = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"])
+        state = x["s0"].clone()
+        od = kda.kda_decode_step(q1, k1, v1, a1, b1, state)
+    side.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    assert torch.equal(od, od_ref) and torch.equal(state, state_ref)
+
+
+def test_concurrent_calls_from_two_threads(kda):
+    """The library keeps no per-call state: two host threads, each on its own
+    stream, reproduce the results of the same calls made one after another."""
+    import threading
+
+    import torch
+
+    inputs = [device_inputs(variant(WORKLOADS[2], index=57 + j), B=1, T=300, H=4) for j in range(2)]
+    refs = [run_prefill(kda, x, x["s0"]) for x in inputs]
+    outs = [None, None]
+    errors = []
+
+    def work(j):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    outs[j] = kda.kda_chunk_fwd(inputs[j]["q"], inputs[j]["k"], inputs[j]["v"], inputs[j]["a"],
+                                                inputs[j]["beta"], initial_state=inputs[j]["s0"])
+            s.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for j in range(2):
+        assert torch.equal(outs[j][0], refs[j][0]) and torch.equal(outs[j][1], refs[j][1])
