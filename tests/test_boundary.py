@@ -166,3 +166,13 @@ def test_binding_rejects_wrong_shapes_and_dtypes(lib):
     args = _decode_args(torch, torch.float16)
     with pytest.raises(TypeError, match="bfloat16 or float32"):
         kda.kda_decode_step(**args)
+
+
+def test_binding_raises_without_the_library(monkeypatch):
+    """No CPU fallback: with the shared library absent every call fails loudly."""
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libkda.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        kda.lib()
+    with pytest.raises(RuntimeError, match="no fallback"):
+        kda.last_error()
