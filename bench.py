@@ -6,9 +6,11 @@ beta and state), inputs already resident in HBM.  Printed as one JSON line:
 value = tokens/s; `roofline` is the prefill kernel against HBM (its binding
 roof); `decode` adds kda_decode_step on the decode workload (256 sequences x
 96 heads, fp32 state updated in place, 64 steps with fresh inputs);
-`cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+`decode_multi` takes the same 64 tokens per state four at a time through
+kda_decode_multi (one state read and write per call); `cpu_baseline` is the
+fp64 oracle timed on a bounded sample on the host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--decode-tokens K]
 """
 import argparse
 import hashlib
@@ -33,6 +35,11 @@ FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * CHUNK * (3 * D + 2 * D)  # 118784
 STATE_BYTES = D * D * 4
 # Decode, per (sequence, head) step: state read + written once, q/k/v/a in, o out.
 DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + BYTES_PER_TOKEN_HEAD_BF16  # 132356
+# fp32 VALU work of one token on one state: x = S^T(alpha k) and y = S^T(alpha q)
+# (d^2 multiply-adds, 2 d^2 flops, each) and S' = Diag(alpha) S + k (beta e)^T
+# (a multiply and a multiply-add, 3 flops, per entry): 7 d^2 flops in all.
+DECODE_FLOPS_PER_UNIT = 7 * D * D  # 114688
+FP32_VALU_PEAK = 157.3e12  # MI355X fp32 vector, flop/s
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "chunk_fwd_bf16_kernel"  # the kernel the bf16 prefill workload runs
@@ -194,6 +201,50 @@ def bench_decode(reps=3):
                 step_bytes=unit_bytes, steps=w.T, reps=reps)
 
 
+def bench_decode_multi(k_tokens, reps=3):
+    """The decode workload's 64 tokens per state taken k_tokens at a time by
+    kda_decode_multi (every token committed): one state read and one write
+    per call instead of per token."""
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+    from synth.workloads import WORKLOADS, device_inputs
+
+    w = WORKLOADS[4]
+    if k_tokens < 1 or w.T % k_tokens:
+        raise SystemExit(f"--decode-tokens must divide the workload's {w.T} tokens")
+    x = device_inputs(w)
+    calls = [{n: x[n][:, t:t + k_tokens].contiguous() for n in ("q", "k", "v", "a", "beta")}
+             for t in range(0, w.T, k_tokens)]
+    for n in ("q", "k", "v", "a", "beta"):
+        del x[n]
+    s0 = x["s0"]
+    state = torch.empty_like(s0)
+    outs = [torch.empty((w.B, c["q"].shape[1], w.H, D), dtype=torch.bfloat16, device="cuda") for c in calls]
+    stream = torch.cuda.current_stream()
+    totals, per_call = [], []
+    for rep in range(reps + 1):
+        state.copy_(s0)  # restore the initial state outside the timed region
+        torch.cuda.synchronize()
+        it = iter(range(len(calls)))
+
+        def one():
+            i = next(it)
+            c = calls[i]
+            kda.kda_decode_multi(c["q"], c["k"], c["v"], c["a"], c["beta"], state, o=outs[i], stream=stream)
+
+        ms = timed_launches(one, len(calls), stream)
+        if rep > 0:
+            totals.append(sum(ms))
+            per_call += ms
+    best = min(totals)
+    avg_call_ms = sum(per_call) / len(per_call)
+    call_bytes = w.B * w.H * (2 * STATE_BYTES + k_tokens * BYTES_PER_TOKEN_HEAD_BF16)
+    call_flops = w.B * w.H * k_tokens * DECODE_FLOPS_PER_UNIT
+    return dict(workload=w, seq_steps_per_s=w.B * w.T / (best / 1e3), avg_call_ms=avg_call_ms,
+                call_bytes=call_bytes, call_flops=call_flops, calls=len(calls), k=k_tokens, reps=reps)
+
+
 def cpu_baseline(threads):
     """The oracle as it stands, on the prefill workload (all 96 heads, all
     8192 tokens: about 30 core-seconds), on `threads` host threads.  Input
@@ -227,6 +278,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--decode-tokens", type=int, default=4,
+                    help="tokens per kda_decode_multi call on the decode workload (1 skips that measurement)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -286,6 +339,21 @@ def main():
                          "frac": dach / HBM_PEAK, "traffic": measured_traffic("decode_kernel"),
                          "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec["step_bytes"]},
         }
+        if args.decode_tokens > 1:
+            torch.cuda.empty_cache()
+            mul = bench_decode_multi(args.decode_tokens)
+            mb = mul["call_bytes"] / (mul["avg_call_ms"] / 1e3)
+            mf = mul["call_flops"] / (mul["avg_call_ms"] / 1e3)
+            result["decode_multi"] = {
+                "workload": mul["workload"].name, "tokens_per_call": mul["k"], "value": mul["seq_steps_per_s"],
+                "unit": "seq-steps/s", "calls": mul["calls"], "reps": mul["reps"], "ms_per_call": mul["avg_call_ms"],
+                "vs_single_step": mul["seq_steps_per_s"] / dec["seq_steps_per_s"],
+                "hbm": {"achieved": mb / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": mb / HBM_PEAK,
+                        "algorithmic_bytes_per_launch": mul["call_bytes"]},
+                "alu": {"achieved": mf / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+                        "frac": mf / FP32_VALU_PEAK, "algorithmic_flops_per_launch": mul["call_flops"]},
+                "kernel": "decode_multi_kernel",
+            }
     if not args.no_cpu:
         threads = max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline(threads)

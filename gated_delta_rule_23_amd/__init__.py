@@ -7,10 +7,13 @@ is no fallback: if libkda.so is missing or was not built, every call raises.
     kda_chunk_fwd(q, k, v, a, beta, initial_state=None, o=None, final_state=None)
         -> (o, final_state)
     kda_decode_step(q, k, v, a, beta, state, o=None) -> o      (state updated in place)
+    kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None) -> o
+        (K tokens per sequence; the state keeps the first n_commit[b] of them)
 
-Layouts (contiguous CUDA tensors): q, k, v, a, o ``[B, T, H, 128]`` (prefill)
-or ``[B, H, 128]`` (decode) in bfloat16 or float32; beta ``[B, T, H]`` /
-``[B, H]`` float32; states ``[B, H, 128, 128]`` float32.
+Layouts (contiguous CUDA tensors): q, k, v, a, o ``[B, T, H, 128]`` (prefill),
+``[B, H, 128]`` (decode) or ``[B, K, H, 128]`` (several tokens) in bfloat16 or
+float32; beta ``[B, T, H]`` / ``[B, H]`` / ``[B, K, H]`` float32; states
+``[B, H, 128, 128]`` float32.
 """
 import ctypes
 import os
@@ -43,6 +46,8 @@ def lib():
         L.kda_chunk_fwd.restype = i
         L.kda_decode_step.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
         L.kda_decode_step.restype = i
+        L.kda_decode_multi.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, p]
+        L.kda_decode_multi.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -153,6 +158,37 @@ def kda_decode_step(q, k, v, a, beta, state, o=None, stream=None):
     return o
 
 
+def kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None, stream=None):
+    """K tokens per sequence in one pass (kda_decode_multi of include/kda.h):
+    q, k, v, a [B, K, H, 128]; beta [B, K, H]; n_commit None (all K) or an
+    int32 GPU tensor [B] of tokens committed to the state, which is updated
+    in place.  Returns o [B, K, H, 128]."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, K, H, 128]")
+    B, K, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _require(q, "q", (B, K, H, Dk), dt, dev)
+    _require(k, "k", (B, K, H, Dk), dt, dev)
+    _require(a, "a", (B, K, H, Dk), dt, dev)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, K, H, Dv]")
+    Dv = v.shape[3]
+    _require(v, "v", (B, K, H, Dv), dt, dev)
+    _require(beta, "beta", (B, K, H), torch.float32, dev)
+    _require(state, "state", (B, H, Dk, Dv), torch.float32, dev)
+    if n_commit is not None:
+        _require(n_commit, "n_commit", (B,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((B, K, H, Dv), dtype=dt, device=dev)
+    _require(o, "o", (B, K, H, Dv), dt, dev)
+    _check(lib().kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(state), _ptr(o),
+                                  _ptr(n_commit), B, K, H, Dk, Dv, code, _stream(dev, stream)))
+    return o
+
+
 def raw_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, stream=0):
     """Direct call of the C entry point with raw integer pointers; returns
     the status code without raising (used by the error-path tests)."""
@@ -161,6 +197,10 @@ def raw_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, 
 
 def raw_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream=0):
     return lib().kda_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream)
+
+
+def raw_decode_multi(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype, stream=0):
+    return lib().kda_decode_multi(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype, stream)
 
 
 def last_error():

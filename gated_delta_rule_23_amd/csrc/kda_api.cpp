@@ -133,6 +133,31 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
   return ok();
 }
 
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                            float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
+                            kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_decode_multi";
+  KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  if (K < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (K=%d)", fn, K);
+  const int64_t units = (int64_t)B * H;
+  if (units == 0 || K == 0) return ok();
+  if ((double)B * (double)K * (double)H * 128.0 > 4.0e18)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*K*H*128 overflows the index range", fn);
+  KDA_TRY(check_ptr(fn, "q", q));
+  KDA_TRY(check_ptr(fn, "k", k));
+  KDA_TRY(check_ptr(fn, "v", v));
+  KDA_TRY(check_ptr(fn, "a", a));
+  KDA_TRY(check_ptr(fn, "beta", beta));
+  KDA_TRY(check_ptr(fn, "state", state));
+  KDA_TRY(check_ptr(fn, "o", o));
+  if (n_commit && (reinterpret_cast<uintptr_t>(n_commit) & 3u) != 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_commit is not 4-byte aligned", fn);
+  hipError_t e = kda::launch_decode_multi(q, k, v, a, beta, state, o, n_commit, (int)units, H, K, dtype == KDA_BF16,
+                                          static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 const char* kda_status_string(kda_status status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";

@@ -132,6 +132,223 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __rest
   }
 }
 
+// ------------------------------------------------------------------ several tokens per state
+// K tokens of each (b, h) in one pass: the state is read once, stepped through
+// the K tokens in registers, and written once, after the first n_commit[b]
+// tokens (or not at all for n_commit[b] = 0); every token's output is
+// written.  This is the replay of an accepted draft prefix that the page
+// "Kimi K3：从三条信息流到完整系统" (section "recurrent speculative decoding
+// 不能复制整个状态") and the page "Kimi K3: Two point eight trillion
+// parameters, open weights, and forty-seven pages of how" (section "The
+// machine underneath") describe: the state after any accepted prefix follows
+// from the cached per-token inputs, and tokens past the prefix are never
+// committed.
+//
+// Layout: a 256-thread workgroup per state, wave w owning columns 32w ..
+// 32w+31 of all 128 rows; lane l holds columns 32w + 4(l%8) .. +3 of rows
+// l/8 + 8m, m = 0..15, so each load or store instruction moves eight whole
+// 128-byte row segments.  A column's sums over the rows (x and y of the step)
+// then stay inside its wave (a DPP rotate and two half swaps), so a token
+// needs no barrier: the waves only share the per-channel values of the
+// tokens, which the workgroup stages in LDS eight tokens at a time (thread t:
+// channel t % 128 of tokens t / 128 + 2i) behind one barrier, and it loads the
+// next group's inputs (or the next state's first group and the state
+// itself) into registers right after staging.
+constexpr int kMultiThreads = 256;
+constexpr int kMultiRows = kD / 8;  // rows per lane
+constexpr int kGroupTokens = 8;     // tokens staged per LDS set
+constexpr int kStagePerThread = kGroupTokens * kD / kMultiThreads;  // 4
+
+__device__ __forceinline__ float sum_row_pairs(float x) {
+  // x + (the lane 8 away within its 16-lane row), then across rows 0-1 / 2-3,
+  // then across the two halves: the sum over lane bits 3, 4 and 5
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Four consecutive output values through a buffer resource: one 8-byte
+// (bf16) or 16-byte (fp32) store.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kNonTemporal = 2;  // buffer access cache policy: the nt bit (the state streams through once)
+template <typename IO>
+__device__ __forceinline__ void store4(rsrc_t r, int off, f32x4 x);
+template <>
+__device__ __forceinline__ void store4<float>(rsrc_t r, int off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(rsrc_t r, int off, f32x4 x) {
+  auto bits = [](float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)f); };  // round to nearest even
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{bits(x[0]) | (bits(x[1]) << 16), bits(x[2]) | (bits(x[3]) << 16)}, r,
+                                        off, 0, 0);
+}
+
+template <typename IO>
+__global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v, const IO* __restrict__ a,
+    const float* __restrict__ beta, float* __restrict__ state, IO* __restrict__ o, const int* __restrict__ n_commit,
+    int units, int H, int K) {
+  // per token and key channel: (alpha k, alpha q) for the sums, (alpha, k) for the update
+  __shared__ f32x2 s_kq[2][kGroupTokens][kD], s_ak[2][kGroupTokens][kD];
+  __shared__ float s_v[2][kGroupTokens][kD];
+  __shared__ float s_beta[2][kGroupTokens], s_qk[2][kGroupTokens][2];
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int c0 = 32 * w + 4 * (lane & 7);  // this lane's four columns
+  const int r0 = lane >> 3;                // and rows r0 + 8m
+  const int sc = t & (kD - 1), sj = t / kD;  // staging: channel sc of tokens sj + 2i
+  // a state through a buffer resource: one 32-bit lane offset, row block m at 4 KiB m
+  const int st_off = (r0 * kD + c0) * (int)sizeof(float);
+  auto state_rsrc = [&](int u) { return make_rsrc(state + (size_t)u * kD * kD, kD * kD * (int64_t)sizeof(float)); };
+  auto load_state = [&](int u, f32x4 (&dst)[kMultiRows]) {
+    const rsrc_t r = state_rsrc(u);
+#pragma unroll
+    for (int m = 0; m < kMultiRows; ++m)
+      dst[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off, 8 * m * kD * (int)sizeof(float),
+                                                                               kNonTemporal));
+  };
+  // Token j of unit u = b H + h is row (b K + j) H + h of the [B, K, H, .]
+  // inputs: a unit's K rows of a tensor are one buffer resource (loads past
+  // its last row return 0), addressed by 32-bit offsets j H 128 + channel.
+  const int tok_elems = H * kD;
+  auto first_row = [&](int u) { return ((size_t)(u / H) * K) * H + (u % H); };
+  auto rows_rsrc = [&](const IO* base, int u) {
+    return make_rsrc(base + first_row(u) * kD, ((int64_t)(K - 1) * tok_elems + kD) * (int64_t)sizeof(IO));
+  };
+  struct Staged {
+    uint32_t q[kStagePerThread], k[kStagePerThread], a[kStagePerThread], v[kStagePerThread];
+    float b[kStagePerThread];
+  };
+  auto load_group = [&](int u, int g, Staged& in) {
+    const rsrc_t rq = rows_rsrc(q, u), rk = rows_rsrc(k, u), ra = rows_rsrc(a, u), rv = rows_rsrc(v, u);
+    const rsrc_t rb = make_rsrc(beta + first_row(u), ((int64_t)(K - 1) * H + 1) * (int64_t)sizeof(float));
+#pragma unroll
+    for (int i = 0; i < kStagePerThread; ++i) {
+      const int j = kGroupTokens * g + sj + 2 * i;
+      const int off = (j * tok_elems + sc) * (int)sizeof(IO);
+      in.q[i] = Raw<IO>::load(rq, off);
+      in.k[i] = Raw<IO>::load(rk, off);
+      in.a[i] = Raw<IO>::load(ra, off);
+      in.v[i] = Raw<IO>::load(rv, off);
+      in.b[i] = load_f32(rb, j * H * (int)sizeof(float));
+    }
+  };
+  auto commit_count = [&](int u) {
+    const int c = n_commit ? n_commit[u / H] : K;
+    return c < 0 ? 0 : (c > K ? K : c);
+  };
+
+  const int ngroups = (K + kGroupTokens - 1) / kGroupTokens;
+  int unit = blockIdx.x;
+  f32x4 s[kMultiRows], sn[kMultiRows];
+  Staged in = {};
+  int nc = 0, nc_next = 0;
+  if (unit < units) {
+    load_state(unit, s);
+    load_group(unit, 0, in);
+    nc = commit_count(unit);
+  }
+  int set = 0;
+  while (unit < units) {
+    const int next = unit + (int)gridDim.x;
+    const rsrc_t o_rsrc = rows_rsrc(o, unit);
+    for (int g = 0; g < ngroups; ++g, set ^= 1) {
+      // per-channel values of this group's tokens (a token's 128 channels span
+      // two waves, so validity is uniform over a wave)
+#pragma unroll
+      for (int i = 0; i < kStagePerThread; ++i) {
+        const int jj = sj + 2 * i;
+        float qk = 0.0f;
+        if (kGroupTokens * g + jj < K) {
+          const float qi = Raw<IO>::f32(in.q[i]), ki = Raw<IO>::f32(in.k[i]), ai = Raw<IO>::f32(in.a[i]);
+          const float al = expf(kGateFloor / (1.0f + expf(-ai)));
+          s_kq[set][jj][sc] = f32x2{al * ki, al * qi};
+          s_ak[set][jj][sc] = f32x2{al, ki};
+          s_v[set][jj][sc] = Raw<IO>::f32(in.v[i]);
+          if (sc == 0) s_beta[set][jj] = in.b[i];
+          qk = qi * ki;
+        }
+        const float d = wave_sum(qk);
+        if (lane == 0) s_qk[set][jj][w & 1] = d;
+      }
+      // inputs of the next group, or of the next state's first group with the state itself
+      if (g + 1 < ngroups) {
+        load_group(unit, g + 1, in);
+      } else if (next < units) {
+        load_group(next, 0, in);
+        load_state(next, sn);
+        nc_next = commit_count(next);
+      }
+      __syncthreads();
+
+      const int jn = K - kGroupTokens * g < kGroupTokens ? K - kGroupTokens * g : kGroupTokens;
+#pragma unroll 1
+      for (int jj = 0; jj < jn; ++jj) {
+        const int j = kGroupTokens * g + jj;
+        // x = S^T (alpha k), y = S^T (alpha q) over this lane's rows, then over the wave's rows
+        f32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < kMultiRows; ++m) {
+          const f32x2 kq = s_kq[set][jj][r0 + 8 * m];
+          x += kq[0] * s[m];
+          y += kq[1] * s[m];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[c] = sum_row_pairs(x[c]);
+          y[c] = sum_row_pairs(y[c]);
+        }
+        const float bt = s_beta[set][jj], qk = s_qk[set][jj][0] + s_qk[set][jj][1];
+        const f32x4 e = *reinterpret_cast<const f32x4*>(&s_v[set][jj][c0]) - x;
+        const f32x4 be = bt * e;
+        if (r0 == 0) store4<IO>(o_rsrc, (j * tok_elems + c0) * (int)sizeof(IO), y + (bt * qk) * e);
+        // S' = Diag(alpha) S + k (beta e)^T
+#pragma unroll
+        for (int m = 0; m < kMultiRows; ++m) {
+          const f32x2 ak = s_ak[set][jj][r0 + 8 * m];
+          s[m] = ak[0] * s[m] + ak[1] * be;
+        }
+        if (j + 1 == nc) {
+          const rsrc_t r = state_rsrc(unit);
+#pragma unroll
+          for (int m = 0; m < kMultiRows; ++m)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), r, st_off,
+                                                   8 * m * kD * (int)sizeof(float), kNonTemporal);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kMultiRows; ++m) s[m] = sn[m];
+    nc = nc_next;
+    unit = next;
+  }
+}
+
+hipError_t launch_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                               float* state, void* o, const int* n_commit, int units, int H, int K, bool bf16_io,
+                               hipStream_t stream) {
+  if (units == 0 || K == 0) return hipSuccess;
+  int cus = 0;
+  const hipError_t err = device_cu_count(stream, &cus);
+  if (err != hipSuccess) return err;
+  // two resident workgroups per compute unit (a wave holds 128 state registers
+  // and as many for the next state's)
+  const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 1);
+  const unsigned grid = (unsigned)(units < slots ? units : slots);
+  if (bf16_io) {
+    hipLaunchKernelGGL(decode_multi_kernel<bf16>, dim3(grid), dim3(kMultiThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o, n_commit, units, H, K);
+  } else {
+    hipLaunchKernelGGL(decode_multi_kernel<float>, dim3(grid), dim3(kMultiThreads), 0, stream, (const float*)q,
+                       (const float*)k, (const float*)v, (const float*)a, beta, state, (float*)o, n_commit, units,
+                       H, K);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
                          void* o, int units, bool bf16_io, hipStream_t stream) {
   if (units == 0) return hipSuccess;

@@ -17,6 +17,12 @@ hipError_t device_cu_count(hipStream_t stream, int* cus);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
                          void* o, int units, bool bf16_io, hipStream_t stream);
 
+/* K tokens per state: q, k, v, a, o are [B, K, H, 128] with units = B * H;
+ * beta [B, K, H]; n_commit [B] (NULL = K) tokens committed to the state. */
+hipError_t launch_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                               float* state, void* o, const int* n_commit, int units, int H, int K, bool bf16_io,
+                               hipStream_t stream);
+
 /* Chunkwise prefill over [B, T, H, 128] rows: fp32 or bf16 I/O (kda_chunk.hip). */
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             const float* initial_state, void* o, float* final_state, int B, int T, int H,

@@ -94,6 +94,40 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype,
                            void* hip_stream);
 
+/*
+ * K tokens of each sequence in one pass, for speculative decoding: the state
+ * is read once, stepped through the tokens in order (each step as in
+ * kda_decode_step), and written once, holding the state after the first
+ * n_commit[b] tokens of batch row b; the tokens after them are never
+ * committed.  Every token's output is written, read from the running state
+ * after that token (so outputs past n_commit[b] are those of the uncommitted
+ * continuation).  The page "Kimi K3：从三条信息流到完整系统" (section
+ * "recurrent speculative decoding 不能复制整个状态") and the page "Kimi K3:
+ * Two point eight trillion parameters, open weights, and forty-seven pages of
+ * how" (section "The machine underneath") describe this replay: cache the
+ * drafted tokens' inputs, verify, then replay only the accepted prefix from
+ * the committed state, with no per-position state snapshots.  Verifying a
+ * draft takes n_commit = 0 (outputs only, state untouched); committing m
+ * accepted tokens takes them again with n_commit = m.
+ *
+ *   q, k, a   [B, K, H, Dk]   dtype   (read)
+ *   v         [B, K, H, Dv]   dtype   (read)
+ *   beta      [B, K, H]       fp32    (read)
+ *   state     [B, H, Dk, Dv]  fp32    (read; overwritten with the state after
+ *                                      n_commit[b] tokens, left untouched where
+ *                                      n_commit[b] = 0)
+ *   o         [B, K, H, Dv]   dtype   (written, all K tokens)
+ *   n_commit  [B] int32 on the device, 4-byte aligned, or NULL for K; values
+ *             outside [0, K] are clamped to it (the library does not read
+ *             device memory on the host, so it cannot reject them)
+ *
+ * K = 0 (or B * H = 0) enqueues nothing.  With K = 1 and n_commit NULL the
+ * result is that of kda_decode_step.
+ */
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                            float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
+                            kda_dtype dtype, void* hip_stream);
+
 /* Static text for a status code. */
 const char* kda_status_string(kda_status status);
 

@@ -16,7 +16,10 @@ Arrays here use the boundary's layouts: rows ``[B, T, H, D]``, beta
 Parity pins: every function here is pinned by the tests in
 ``tests/test_oracle_pins.py`` (worked example, hand-solved scalar case, erase
 identity, beta = 0 and beta -> 0 closed forms, basis-key overwrite, dense
-unrolled products with segment composition, gate bound, split invariance).
+unrolled products with segment composition, gate bound, split invariance;
+for ``decode_multi`` a hand-solved two-token commit, the beta = 0 closed form
+at every commit count, and that tokens past the committed prefix change
+neither the committed state nor earlier outputs).
 """
 import ctypes
 import os
@@ -112,3 +115,31 @@ def decode_step(q, k, v, beta, state, a=None, g=None, threads=None):
                    a=None if a is None else a[:, None], g=None if g is None else g[:, None], s0=state,
                    threads=threads)
     return o[:, 0], S
+
+
+def decode_multi(q, k, v, beta, state, a=None, g=None, n_commit=None, threads=None):
+    """K tokens per (b, h) from a committed state, the replay of an accepted
+    draft prefix (page "Kimi K3：从三条信息流到完整系统", section "recurrent
+    speculative decoding 不能复制整个状态": the drafted tokens' inputs are
+    cached and only the accepted prefix is replayed into the state; the rest
+    is never committed).
+
+    q, k, v, a|g [B, K, H, D]; beta [B, K, H]; state [B, H, Dk, Dv];
+    n_commit [B] token counts (None = K), clamped to [0, K].  Returns
+    (o [B, K, H, Dv] for every token, read from the running state after that
+    token; the state after the first n_commit[b] tokens of batch row b)."""
+    o, _ = forward(q, k, v, beta, a=a, g=g, s0=state, threads=threads)
+    B, K = q.shape[0], q.shape[1]
+    counts = np.full(B, K) if n_commit is None else np.clip(np.asarray(n_commit).reshape(B), 0, K)
+    committed = np.array(state, dtype=np.float64, copy=True)
+    gv = a if a is not None else g
+    for b in range(B):
+        m = int(counts[b])
+        if m == 0:
+            continue
+        sl = slice(b, b + 1)
+        kw = {"a": gv[sl, :m]} if a is not None else {"g": gv[sl, :m]}
+        _, Sb = forward(q[sl, :m], k[sl, :m], v[sl, :m], np.asarray(beta)[sl, :m], s0=np.asarray(state)[sl],
+                        threads=threads, **kw)
+        committed[b] = Sb[0]
+    return o, committed

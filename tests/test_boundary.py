@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error", "kda_version"):
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_decode_multi", "kda_status_string", "kda_last_error",
+              "kda_version"):
         assert n in names
 
 
@@ -63,6 +64,13 @@ def decode(**kw):
     return kda.raw_decode_step(*args.values())
 
 
+def multi(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, state=P, o=P, n_commit=None, B=1, K=4, H=1, Dk=128, Dv=128,
+                dtype=kda.KDA_BF16)
+    args.update(kw)
+    return kda.raw_decode_multi(*args.values())
+
+
 @pytest.mark.parametrize("field", ["q", "k", "v", "a", "beta", "o", "final_state"])
 def test_chunk_rejects_null_pointers(lib, field):
     assert chunk(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT
@@ -79,6 +87,35 @@ def test_chunk_rejects_misaligned_pointers(lib, field):
 def test_decode_rejects_null_and_misaligned(lib, field):
     assert decode(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT
     assert decode(**{field: MIS}) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "a", "beta", "state", "o"])
+def test_multi_rejects_null_and_misaligned(lib, field):
+    assert multi(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert field in kda.last_error()
+    assert multi(**{field: MIS}) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "aligned" in kda.last_error()
+
+
+def test_multi_commit_counts_need_only_int_alignment(lib):
+    # n_commit is an int32 array: 4-byte alignment is enough, less is rejected
+    assert multi(n_commit=P + 2, K=1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "n_commit" in kda.last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(K=-1), dict(H=-2), dict(Dk=0), dict(dtype=7)])
+def test_multi_rejects_bad_sizes_and_enums(lib, kw):
+    assert multi(**kw) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_multi_limits_and_no_ops(lib):
+    assert multi(Dv=64) == kda.KDA_ERR_UNSUPPORTED
+    assert multi(B=(1 << 31) - (1 << 20) + 1, H=1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert multi(B=1 << 20, K=1 << 30, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT  # B*K*H*128 > 2^62
+    assert "overflow" in kda.last_error()
+    # nothing to do: no tokens, or no sequences; NULL pointers allowed
+    assert kda.raw_decode_multi(None, None, None, None, None, None, None, None, 2, 0, 4, 128, 128, 1) == kda.KDA_OK
+    assert kda.raw_decode_multi(None, None, None, None, None, None, None, None, 0, 4, 4, 128, 128, 0) == kda.KDA_OK
 
 
 @pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=-2), dict(Dk=0), dict(Dv=-128), dict(dtype=7)])
@@ -146,13 +183,20 @@ def _chunk_args(torch, dtype):
                 beta=torch.zeros(B, T, H))
 
 
-@pytest.mark.parametrize("entry", ["decode", "chunk"])
+def _multi_args(torch, dtype):
+    B, K, H, D = 2, 3, 2, 128
+    return dict(q=torch.zeros(B, K, H, D, dtype=dtype), k=torch.zeros(B, K, H, D, dtype=dtype),
+                v=torch.zeros(B, K, H, D, dtype=dtype), a=torch.zeros(B, K, H, D, dtype=dtype),
+                beta=torch.zeros(B, K, H), state=torch.zeros(B, H, D, D))
+
+
+@pytest.mark.parametrize("entry", ["decode", "chunk", "multi"])
 def test_binding_rejects_host_tensors_before_any_call(lib, entry):
     """Host (CPU) tensors never reach the C ABI: their addresses are not
     device pointers.  Every tensor argument is checked, q included."""
     torch = pytest.importorskip("torch")
-    args = (_decode_args if entry == "decode" else _chunk_args)(torch, torch.float32)
-    fn = kda.kda_decode_step if entry == "decode" else kda.kda_chunk_fwd
+    args = {"decode": _decode_args, "chunk": _chunk_args, "multi": _multi_args}[entry](torch, torch.float32)
+    fn = {"decode": kda.kda_decode_step, "chunk": kda.kda_chunk_fwd, "multi": kda.kda_decode_multi}[entry]
     with pytest.raises(ValueError, match="q must be a GPU tensor"):
         fn(**args)
 

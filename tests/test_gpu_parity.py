@@ -5,6 +5,8 @@ oracle on everything; the full-size workloads are checked on sampled heads
 (whole sequences), or on token windows whose entering state is provably
 forgotten (see test_workload3_full_size_windows)."""
 import numpy as np
+import oracle
+import synth
 import pytest
 
 from tests.conftest import gpu_available
@@ -358,6 +360,124 @@ def test_decode_empty_batch_is_a_no_op(kda):
     s = torch.empty((0, 4, 128, 128), dtype=torch.float32, device="cuda")
     o = kda.kda_decode_step(z, z, z, z, torch.empty((0, 4), device="cuda"), s)
     assert o.shape == (0, 4, 128)
+
+
+# --------------------------------------------------------------------------- several tokens per state
+
+
+def _multi_oracle(w, B, K, H, n_commit):
+    """The oracle's replay of K tokens of workload w from its initial state."""
+    h = host_inputs(w, nb=B, nt=K, nh=H)
+    return oracle.decode_multi(synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]),
+                               h["beta"].astype(np.float64), h["s0"].astype(np.float64), a=synth.to_f64(h["a"]),
+                               n_commit=n_commit)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 3, 8, 13])
+def test_decode_multi_against_oracle(kda, dtype, K):
+    """K tokens per state in one call: every token's output and the state
+    after each batch row's committed prefix (all, none, about half), against
+    the oracle.  K = 13 takes two token groups, the second ragged."""
+    import torch
+
+    w = variant(WORKLOADS[4], index=80 + K, dtype=dtype)
+    B, H = 3, 5
+    counts = [K, 0, K // 2]
+    print_case(f"case decode multi {dtype} B={B} K={K} H={H} n_commit={counts}")
+    x = device_inputs(w, B=B, T=K, H=H)
+    state = x["s0"].clone()
+    nc = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    o = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], state, n_commit=nc)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _multi_oracle(w, B, K, H, counts)
+    eo, es = rel_l2(to_np(o), o_ref), rel_l2(to_np(state), S_ref)
+    print_case(f"  rel_l2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    # the row that commits nothing keeps its state bit for bit
+    assert torch.equal(state[1], x["s0"][1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_multi_one_token_is_a_decode_step(kda, dtype):
+    import torch
+
+    w = variant(WORKLOADS[4], index=90, dtype=dtype)
+    B, H = 4, 7
+    x = device_inputs(w, B=B, T=1, H=H)
+    s1, s2 = x["s0"].clone(), x["s0"].clone()
+    o1 = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], s1)
+    o2 = kda.kda_decode_step(x["q"][:, 0].contiguous(), x["k"][:, 0].contiguous(), x["v"][:, 0].contiguous(),
+                             x["a"][:, 0].contiguous(), x["beta"][:, 0].contiguous(), s2)
+    torch.cuda.synchronize()
+    assert rel_l2(to_np(o1[:, 0]), to_np(o2)) <= 1e-6 and rel_l2(to_np(s1), to_np(s2)) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_multi_grid_stride_ragged_counts(kda, dtype):
+    """27 x 97 = 2619 states over two workgroups per compute unit, so each
+    workgroup replays several states and prefetches the next one's state and
+    first token group; per-row counts cover 0..K and out-of-range values,
+    which are clamped.  Every state is checked on its own."""
+    import torch
+
+    w = variant(WORKLOADS[4], index=91, dtype=dtype)
+    B, K, H = 27, 5, 97
+    counts = [(-2 if b % 9 == 0 else (K + 3 if b % 9 == 1 else b % (K + 1))) for b in range(B)]
+    print_case(f"case decode multi grid stride {dtype} B={B} K={K} H={H}")
+    x = device_inputs(w, B=B, T=K, H=H)
+    state = x["s0"].clone()
+    o = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], state,
+                             n_commit=torch.tensor(counts, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    o_ref, S_ref = _multi_oracle(w, B, K, H, counts)
+    S, on = to_np(state), to_np(o)
+    num_s = np.sqrt(((S - S_ref) ** 2).sum(axis=(2, 3)))
+    den_s = np.sqrt((S_ref ** 2).sum(axis=(2, 3)))
+    num_o = np.sqrt(((on - o_ref) ** 2).sum(axis=(1, 3)))
+    den_o = np.sqrt((o_ref ** 2).sum(axis=(1, 3)))
+    worst_s, worst_o = float((num_s / den_s).max()), float((num_o / den_o).max())
+    print_case(f"  worst per-state rel_l2 S={worst_s:.3e} o={worst_o:.3e}")
+    assert worst_s <= TOL[dtype] and worst_o <= TOL[dtype]
+    uncommitted = [b for b in range(B) if counts[b] <= 0]
+    assert torch.equal(state[uncommitted], x["s0"][uncommitted])
+
+
+def test_decode_multi_verify_then_commit(kda):
+    """The speculative flow: verify K drafted tokens without committing
+    (n_commit = 0: outputs only, state untouched), then replay the accepted
+    prefix of m tokens with n_commit = m; the state equals m decode steps."""
+    import torch
+
+    w = variant(WORKLOADS[4], index=92, dtype="bf16")
+    B, K, H = 2, 6, 4
+    x = device_inputs(w, B=B, T=K, H=H)
+    state = x["s0"].clone()
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    o_draft = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], state, n_commit=zero)
+    torch.cuda.synchronize()
+    assert torch.equal(state, x["s0"])
+    m = 4
+    sub = {n: x[n][:, :m].contiguous() for n in ("q", "k", "v", "a", "beta")}
+    o_acc = kda.kda_decode_multi(sub["q"], sub["k"], sub["v"], sub["a"], sub["beta"], state,
+                                 n_commit=torch.full((B,), m, dtype=torch.int32, device="cuda"))
+    ref = x["s0"].clone()
+    steps = [kda.kda_decode_step(*(x[n][:, t].contiguous() for n in ("q", "k", "v", "a", "beta")), ref)
+             for t in range(m)]
+    torch.cuda.synchronize()
+    assert torch.equal(o_acc, o_draft[:, :m])  # same arithmetic on the same prefix
+    assert rel_l2(to_np(state), to_np(ref)) <= 1e-6
+    assert rel_l2(to_np(torch.stack(steps, dim=1)), to_np(o_acc)) <= 1e-6
+
+
+def test_decode_multi_empty_is_a_no_op(kda):
+    import torch
+
+    z = torch.empty((2, 0, 3, 128), dtype=torch.bfloat16, device="cuda")
+    s = torch.zeros((2, 3, 128, 128), dtype=torch.float32, device="cuda")
+    o = kda.kda_decode_multi(z, z, z, z, torch.empty((2, 0, 3), device="cuda"), s)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 128) and not s.any()
 
 
 # --------------------------------------------------------------------------- streams and threads

@@ -67,6 +67,68 @@ def test_decode_step_is_one_token_of_forward():
     assert np.array_equal(S, S_ref)
 
 
+def test_decode_multi_hand_solved_two_tokens():
+    """Two tokens with orthonormal keys, beta = 1 and no decay (g = 0), solved
+    by hand from eq. (1): token 1 writes v1 under e1 (S1 = e1 v1^T), token 2
+    writes v2 under e2 (S2 = e1 v1^T + e2 v2^T); o_t = S_t^T q_t.  Committing
+    one token keeps S1, none keeps S0 = 0, both keep S2."""
+    d = 4
+    e1, e2 = np.eye(d)[0], np.eye(d)[1]
+    v1, v2 = np.array([1.0, -2.0, 0.5, 3.0]), np.array([0.25, 4.0, -1.0, 2.0])
+    q1, q2 = np.array([2.0, 7.0, 0.0, -1.0]), np.array([-3.0, 0.5, 9.0, 1.0])
+    q = np.stack([q1, q2])[None, :, None]  # [B=1, K=2, H=1, d]
+    k = np.stack([e1, e2])[None, :, None]
+    v = np.stack([v1, v2])[None, :, None]
+    g = np.zeros_like(q)
+    beta = np.ones((1, 2, 1))
+    s0 = np.zeros((1, 1, d, d))
+    S1, S2 = np.outer(e1, v1), np.outer(e1, v1) + np.outer(e2, v2)
+    for m, want in ((0, np.zeros((d, d))), (1, S1), (2, S2)):
+        o, S = oracle.decode_multi(q, k, v, beta, s0, g=g, n_commit=[m])
+        assert np.allclose(o[0, 0, 0], q1[0] * v1, rtol=0, atol=1e-15)
+        assert np.allclose(o[0, 1, 0], q2[0] * v1 + q2[1] * v2, rtol=0, atol=1e-15)
+        assert np.allclose(S[0, 0], want, rtol=0, atol=1e-15)
+    # counts outside [0, K] are clamped
+    assert np.array_equal(oracle.decode_multi(q, k, v, beta, s0, g=g, n_commit=[-3])[1], s0)
+    assert np.allclose(oracle.decode_multi(q, k, v, beta, s0, g=g, n_commit=[9])[1][0, 0], S2, rtol=0, atol=1e-15)
+
+
+def test_decode_multi_beta_zero_closed_form():
+    """beta = 0 and g = 0 make every step the identity on S (eq. (1)), so
+    o_t = S0^T q_t for every token and the committed state is S0 at every
+    commit count."""
+    rng = np.random.default_rng(21)
+    B, K, H, d = 3, 5, 2, 6
+    q, k, v = (rng.standard_normal((B, K, H, d)) for _ in range(3))
+    s0 = rng.standard_normal((B, H, d, d))
+    o, S = oracle.decode_multi(q, k, v, np.zeros((B, K, H)), s0, g=np.zeros((B, K, H, d)), n_commit=[0, 2, 5])
+    assert np.allclose(o, np.einsum("bhij,bkhi->bkhj", s0, q), rtol=1e-13, atol=1e-13)
+    assert np.allclose(S, s0, rtol=1e-13, atol=1e-13)
+
+
+def test_decode_multi_uncommitted_tokens_change_nothing_committed():
+    """The committed state after m tokens, and the outputs of tokens before t,
+    do not depend on the inputs of later tokens; n_commit = 0 returns the
+    state bit for bit."""
+    rng = np.random.default_rng(22)
+    B, K, H, d = 2, 6, 2, 8
+    q, k, v, a = (rng.standard_normal((B, K, H, d)) for _ in range(4))
+    beta = rng.random((B, K, H))
+    s0 = rng.standard_normal((B, H, d, d))
+    counts = [3, 0]
+    o, S = oracle.decode_multi(q, k, v, beta, s0, a=a, n_commit=counts)
+    assert np.array_equal(S[1], s0[1])
+    q2, k2, v2, a2 = (x.copy() for x in (q, k, v, a))
+    beta2 = beta.copy()
+    for x in (q2, k2, v2, a2):
+        x[:, 3:] = rng.standard_normal(x[:, 3:].shape)
+    beta2[:, 3:] = rng.random(beta2[:, 3:].shape)
+    o2, S2 = oracle.decode_multi(q2, k2, v2, beta2, s0, a=a2, n_commit=counts)
+    assert np.array_equal(S2, S)
+    assert np.array_equal(o2[:, :3], o[:, :3])
+    assert not np.allclose(o2[:, 3:], o[:, 3:])
+
+
 def test_empty_sequence_returns_initial_state():
     rng = np.random.default_rng(14)
     s0 = rng.standard_normal((2, 4, 4))
