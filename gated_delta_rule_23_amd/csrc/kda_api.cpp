@@ -143,6 +143,9 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
   if (units == 0 || K == 0) return ok();
   if ((double)B * (double)K * (double)H * 128.0 > 4.0e18)
     return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*K*H*128 overflows the index range", fn);
+  // the K rows of one (b, h) in one tensor are addressed with 32-bit byte offsets
+  if ((int64_t)K * H * 128 * 4 > INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: K*H=%lld exceeds the limit of %d", fn, (long long)K * H, INT32_MAX / 512);
   KDA_TRY(check_ptr(fn, "q", q));
   KDA_TRY(check_ptr(fn, "k", k));
   KDA_TRY(check_ptr(fn, "v", v));

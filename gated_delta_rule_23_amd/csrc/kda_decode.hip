@@ -150,10 +150,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __rest
 // 128-byte row segments.  A column's sums over the rows (x and y of the step)
 // then stay inside its wave (a DPP rotate and two half swaps), so a token
 // needs no barrier: the waves only share the per-channel values of the
-// tokens, which the workgroup stages in LDS eight tokens at a time (thread t:
-// channel t % 128 of tokens t / 128 + 2i) behind one barrier, and it loads the
-// next group's inputs (or the next state's first group and the state
-// itself) into registers right after staging.
+// tokens, which the workgroup stages in LDS eight tokens at a time behind one
+// barrier (thread t: channel t / 2, tokens 4 (t % 2) .. +3 of the group), and
+// it loads the next group's inputs (or the next state's first group and the
+// state itself) into registers right after staging.
+//
+// Within a group the registers hold T = Diag(1/D_j) S_j, where D_j is the
+// product of the decays alpha of the group's tokens up to j (per key channel;
+// each token's log-decay is at least -5, so D_j >= e^-40 over eight tokens).
+// Since Diag(alpha_j) S_{j-1} = Diag(D_j) T_{j-1}, the step reads
+//   x = T^T (D_j k_j),  y = T^T (D_j q_j),  T += (k_j / D_j) (beta e)^T,
+// one multiply-add per state entry instead of a multiply and a multiply-add;
+// S = Diag(D_j) T is formed only where it is needed: at the group's end
+// before the next group, and for the committed state.
 constexpr int kMultiThreads = 256;
 constexpr int kMultiRows = kD / 8;  // rows per lane
 constexpr int kGroupTokens = 8;     // tokens staged per LDS set
@@ -167,6 +176,13 @@ __device__ __forceinline__ float sum_row_pairs(float x) {
   x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// The sum over the 32 lanes of a wave with the same lane parity.
+__device__ __forceinline__ float sum_same_parity(float x) {
+#pragma unroll
+  for (int off = 2; off <= 32; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
 }
 
 // Four consecutive output values through a buffer resource: one 8-byte
@@ -191,15 +207,16 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v, const IO* __restrict__ a,
     const float* __restrict__ beta, float* __restrict__ state, IO* __restrict__ o, const int* __restrict__ n_commit,
     int units, int H, int K) {
-  // per token and key channel: (alpha k, alpha q) for the sums, (alpha, k) for the update
-  __shared__ f32x2 s_kq[2][kGroupTokens][kD], s_ak[2][kGroupTokens][kD];
+  // per token and key channel: (D k, D q) for the sums, (k / D, D) for the update and the rescale
+  __shared__ f32x2 s_kq[2][kGroupTokens][kD], s_kd[2][kGroupTokens][kD];
   __shared__ float s_v[2][kGroupTokens][kD];
-  __shared__ float s_beta[2][kGroupTokens], s_qk[2][kGroupTokens][2];
+  __shared__ float s_beta[2][kGroupTokens];
+  __shared__ f32x4 s_qk[2][kGroupTokens];  // q . k, one partial sum per wave
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int c0 = 32 * w + 4 * (lane & 7);  // this lane's four columns
   const int r0 = lane >> 3;                // and rows r0 + 8m
-  const int sc = t & (kD - 1), sj = t / kD;  // staging: channel sc of tokens sj + 2i
+  const int sc = t >> 1, sh = t & 1;       // staging: channel sc, tokens 4 sh + i
   // a state through a buffer resource: one 32-bit lane offset, row block m at 4 KiB m
   const int st_off = (r0 * kD + c0) * (int)sizeof(float);
   auto state_rsrc = [&](int u) { return make_rsrc(state + (size_t)u * kD * kD, kD * kD * (int64_t)sizeof(float)); };
@@ -227,7 +244,7 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
     const rsrc_t rb = make_rsrc(beta + first_row(u), ((int64_t)(K - 1) * H + 1) * (int64_t)sizeof(float));
 #pragma unroll
     for (int i = 0; i < kStagePerThread; ++i) {
-      const int j = kGroupTokens * g + sj + 2 * i;
+      const int j = kGroupTokens * g + kStagePerThread * sh + i;
       const int off = (j * tok_elems + sc) * (int)sizeof(IO);
       in.q[i] = Raw<IO>::load(rq, off);
       in.k[i] = Raw<IO>::load(rk, off);
@@ -256,23 +273,31 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
     const int next = unit + (int)gridDim.x;
     const rsrc_t o_rsrc = rows_rsrc(o, unit);
     for (int g = 0; g < ngroups; ++g, set ^= 1) {
-      // per-channel values of this group's tokens (a token's 128 channels span
-      // two waves, so validity is uniform over a wave)
+      // Stage the group's per-channel values.  Tokens past K load as zeros
+      // and are never read back.  log2 D is the running sum of
+      // g log2(e) = -5 log2(e) sigmoid(a) over the group's tokens; the lane
+      // with the later four tokens adds its partner's (lane - 1) total.
+      float lg[kStagePerThread], run = 0.0f;
 #pragma unroll
       for (int i = 0; i < kStagePerThread; ++i) {
-        const int jj = sj + 2 * i;
-        float qk = 0.0f;
-        if (kGroupTokens * g + jj < K) {
-          const float qi = Raw<IO>::f32(in.q[i]), ki = Raw<IO>::f32(in.k[i]), ai = Raw<IO>::f32(in.a[i]);
-          const float al = expf(kGateFloor / (1.0f + expf(-ai)));
-          s_kq[set][jj][sc] = f32x2{al * ki, al * qi};
-          s_ak[set][jj][sc] = f32x2{al, ki};
-          s_v[set][jj][sc] = Raw<IO>::f32(in.v[i]);
-          if (sc == 0) s_beta[set][jj] = in.b[i];
-          qk = qi * ki;
-        }
-        const float d = wave_sum(qk);
-        if (lane == 0) s_qk[set][jj][w & 1] = d;
+        const float ai = Raw<IO>::f32(in.a[i]);
+        run += kGateFloor * kLog2e / (1.0f + expf(-ai));
+        lg[i] = run;
+      }
+      const float before = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(run), 0xB1, 0xf, 0xf, false));
+      const float carry = sh ? before : 0.0f;  // quad_perm [1, 0, 3, 2]: the partner lane's total
+#pragma unroll
+      for (int i = 0; i < kStagePerThread; ++i) {
+        const int jj = kStagePerThread * sh + i;
+        const float qi = Raw<IO>::f32(in.q[i]), ki = Raw<IO>::f32(in.k[i]);
+        const float l2d = lg[i] + carry;
+        const float dd = exp2f(l2d), di = exp2f(-l2d);
+        s_kq[set][jj][sc] = f32x2{dd * ki, dd * qi};
+        s_kd[set][jj][sc] = f32x2{ki * di, dd};
+        s_v[set][jj][sc] = Raw<IO>::f32(in.v[i]);
+        if (sc == 0) s_beta[set][jj] = in.b[i];
+        const float part = sum_same_parity(qi * ki);
+        if (lane < 2) s_qk[set][jj][w] = part;
       }
       // inputs of the next group, or of the next state's first group with the state itself
       if (g + 1 < ngroups) {
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
 #pragma unroll 1
       for (int jj = 0; jj < jn; ++jj) {
         const int j = kGroupTokens * g + jj;
-        // x = S^T (alpha k), y = S^T (alpha q) over this lane's rows, then over the wave's rows
+        // x = T^T (D k), y = T^T (D q) over this lane's rows, then over the wave's rows
         f32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < kMultiRows; ++m) {
@@ -301,23 +326,30 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
           x[c] = sum_row_pairs(x[c]);
           y[c] = sum_row_pairs(y[c]);
         }
-        const float bt = s_beta[set][jj], qk = s_qk[set][jj][0] + s_qk[set][jj][1];
+        const f32x4 qk4 = s_qk[set][jj];
+        const float bt = s_beta[set][jj], qk = (qk4[0] + qk4[1]) + (qk4[2] + qk4[3]);
         const f32x4 e = *reinterpret_cast<const f32x4*>(&s_v[set][jj][c0]) - x;
         const f32x4 be = bt * e;
         if (r0 == 0) store4<IO>(o_rsrc, (j * tok_elems + c0) * (int)sizeof(IO), y + (bt * qk) * e);
-        // S' = Diag(alpha) S + k (beta e)^T
+        // T += (k / D) (beta e)^T
 #pragma unroll
-        for (int m = 0; m < kMultiRows; ++m) {
-          const f32x2 ak = s_ak[set][jj][r0 + 8 * m];
-          s[m] = ak[0] * s[m] + ak[1] * be;
-        }
-        if (j + 1 == nc) {
+        for (int m = 0; m < kMultiRows; ++m) s[m] += s_kd[set][jj][r0 + 8 * m][0] * be;
+        if (j + 1 == nc) {  // commit S = Diag(D) T
+          // The whole offset goes in the lane offset and soffset stays 0: a
+          // 16-byte buffer store with a register soffset was seen to store
+          // its last dword after the next instruction had overwritten it
+          // (the compiler inserts no wait for that form), and with soffset 0
+          // the compiler keeps the store's data registers intact.
           const rsrc_t r = state_rsrc(unit);
 #pragma unroll
           for (int m = 0; m < kMultiRows; ++m)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), r, st_off,
-                                                   8 * m * kD * (int)sizeof(float), kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s_kd[set][jj][r0 + 8 * m][1] * s[m]), r,
+                                                   st_off + 8 * m * kD * (int)sizeof(float), 0, kNonTemporal);
         }
+      }
+      if (g + 1 < ngroups) {  // S = Diag(D) T enters the next group
+#pragma unroll
+        for (int m = 0; m < kMultiRows; ++m) s[m] *= s_kd[set][kGroupTokens - 1][r0 + 8 * m][1];
       }
     }
 #pragma unroll

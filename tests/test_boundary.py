@@ -111,6 +111,8 @@ def test_multi_rejects_bad_sizes_and_enums(lib, kw):
 def test_multi_limits_and_no_ops(lib):
     assert multi(Dv=64) == kda.KDA_ERR_UNSUPPORTED
     assert multi(B=(1 << 31) - (1 << 20) + 1, H=1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert multi(K=1 << 12, H=1 << 10) == kda.KDA_ERR_UNSUPPORTED  # a sequence's K rows span 2^31 bytes
+    assert "K*H" in kda.last_error()
     assert multi(B=1 << 20, K=1 << 30, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT  # B*K*H*128 > 2^62
     assert "overflow" in kda.last_error()
     # nothing to do: no tokens, or no sequences; NULL pointers allowed
