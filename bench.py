@@ -350,6 +350,7 @@ def main():
                 "vs_single_step": mul["seq_steps_per_s"] / dec["seq_steps_per_s"],
                 "hbm": {"achieved": mb / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": mb / HBM_PEAK,
                         "algorithmic_bytes_per_launch": mul["call_bytes"]},
+                "traffic": measured_traffic("decode_multi_kernel"),
                 "alu": {"achieved": mf / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
                         "frac": mf / FP32_VALU_PEAK, "algorithmic_flops_per_launch": mul["call_flops"]},
                 "kernel": "decode_multi_kernel",
