@@ -19,7 +19,9 @@ identity, beta = 0 and beta -> 0 closed forms, basis-key overwrite, dense
 unrolled products with segment composition, gate bound, split invariance;
 for ``decode_multi`` a hand-solved two-token commit, the beta = 0 closed form
 at every commit count, and that tokens past the committed prefix change
-neither the committed state nor earlier outputs).
+neither the committed state nor earlier outputs; for the state checkpoints
+of ``forward(..., state_every=E)`` the beta = 0 closed form, agreement with
+runs over each prefix, and split runs resumed from a checkpoint).
 """
 import ctypes
 import os
@@ -40,6 +42,8 @@ def _load():
         p, i = ctypes.c_void_p, ctypes.c_int
         lib.kda_oracle_forward.argtypes = [i, i, i, i, p, p, p, p, i, p, p, p, p, i]
         lib.kda_oracle_forward.restype = i
+        lib.kda_oracle_forward_states.argtypes = [i, i, i, i, p, p, p, p, i, p, p, p, p, p, i, i]
+        lib.kda_oracle_forward_states.restype = i
         lib.kda_oracle_gate.argtypes = [p, p, ctypes.c_int64]
         lib.kda_oracle_gate.restype = None
         _lib = lib
@@ -62,9 +66,11 @@ def gate(a):
     return g
 
 
-def forward_units(q, k, v, gate_values, beta, s0=None, gate_is_logit=True, threads=None):
+def forward_units(q, k, v, gate_values, beta, s0=None, gate_is_logit=True, threads=None, state_every=None):
     """Unit-major entry: q, k, gate [n, T, Dk]; v [n, T, Dv]; beta [n, T];
-    s0 [n, Dk, Dv] or None.  Returns (o [n, T, Dv], S [n, Dk, Dv])."""
+    s0 [n, Dk, Dv] or None.  Returns (o [n, T, Dv], S [n, Dk, Dv]), and with
+    state_every = E also the checkpoints [n, T // E, Dk, Dv]: the state after
+    tokens E, 2E, ..."""
     q, k, v, gv, beta = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, gate_values, beta))
     n, T, dk = q.shape
     dv = v.shape[2]
@@ -74,12 +80,23 @@ def forward_units(q, k, v, gate_values, beta, s0=None, gate_is_logit=True, threa
         assert s0.shape == (n, dk, dv)
     o = np.empty((n, T, dv), dtype=np.float64)
     S = np.empty((n, dk, dv), dtype=np.float64)
-    rc = _load().kda_oracle_forward(n, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(gv), int(bool(gate_is_logit)),
-                                    _ptr(beta), _ptr(s0), _ptr(o), _ptr(S),
-                                    default_threads() if threads is None else int(threads))
+    nthreads = default_threads() if threads is None else int(threads)
+    if state_every is None:
+        rc = _load().kda_oracle_forward(n, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(gv), int(bool(gate_is_logit)),
+                                        _ptr(beta), _ptr(s0), _ptr(o), _ptr(S), nthreads)
+        if rc != 0:
+            raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
+        return o, S
+    every = int(state_every)
+    if every <= 0:
+        raise ValueError("state_every must be positive")
+    states = np.empty((n, T // every, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_forward_states(n, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(gv),
+                                           int(bool(gate_is_logit)), _ptr(beta), _ptr(s0), _ptr(o), _ptr(S),
+                                           _ptr(states), every, nthreads)
     if rc != 0:
-        raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
-    return o, S
+        raise RuntimeError(f"kda_oracle_forward_states failed with code {rc}")
+    return o, S, states
 
 
 def _units(x):
@@ -91,21 +108,27 @@ def _units(x):
     return np.ascontiguousarray(x.transpose(0, 2, 1)).reshape(B * H, T)
 
 
-def forward(q, k, v, beta, a=None, g=None, s0=None, threads=None):
+def forward(q, k, v, beta, a=None, g=None, s0=None, threads=None, state_every=None):
     """Boundary-layout entry.  q, k, v and a (gate logits) or g (log-decays)
     are [B, T, H, D]; beta [B, T, H]; s0 [B, H, Dk, Dv] or None.
-    Returns (o [B, T, H, Dv], S_final [B, H, Dk, Dv]) in fp64."""
+    Returns (o [B, T, H, Dv], S_final [B, H, Dk, Dv]) in fp64, and with
+    state_every = E also the state checkpoints [B, H, T // E, Dk, Dv] (the
+    state after tokens E, 2E, ..., the sparse KDA checkpoints of the K3
+    page's section "hybrid prefix cache")."""
     if (a is None) == (g is None):
         raise ValueError("pass exactly one of a (gate logits) or g (log-decay)")
     B, T, H, dk = q.shape
     dv = v.shape[3]
     gv = a if a is not None else g
     s0u = None if s0 is None else np.asarray(s0, dtype=np.float64).reshape(B * H, dk, dv)
-    o, S = forward_units(_units(np.asarray(q, np.float64)), _units(np.asarray(k, np.float64)),
-                         _units(np.asarray(v, np.float64)), _units(np.asarray(gv, np.float64)),
-                         _units(np.asarray(beta, np.float64)), s0u, gate_is_logit=a is not None, threads=threads)
-    o = o.reshape(B, H, T, dv).transpose(0, 2, 1, 3)
-    return np.ascontiguousarray(o), S.reshape(B, H, dk, dv)
+    res = forward_units(_units(np.asarray(q, np.float64)), _units(np.asarray(k, np.float64)),
+                        _units(np.asarray(v, np.float64)), _units(np.asarray(gv, np.float64)),
+                        _units(np.asarray(beta, np.float64)), s0u, gate_is_logit=a is not None, threads=threads,
+                        state_every=state_every)
+    o = np.ascontiguousarray(res[0].reshape(B, H, T, dv).transpose(0, 2, 1, 3))
+    if state_every is None:
+        return o, res[1].reshape(B, H, dk, dv)
+    return o, res[1].reshape(B, H, dk, dv), res[2].reshape(B, H, T // int(state_every), dk, dv)
 
 
 def decode_step(q, k, v, beta, state, a=None, g=None, threads=None):

@@ -25,6 +25,11 @@
  * S has d_k rows (key channels) and d_v columns, stored row-major.
  * Layouts: q, k, g|a [n][T][d_k]; v, o [n][T][d_v]; beta [n][T];
  * s0, s_final [n][d_k][d_v] (s0 may be NULL for a zero initial state).
+ *
+ * Optionally the state is also copied out after every `every` tokens (the
+ * sparse KDA state checkpoints of the page's section "hybrid prefix cache"):
+ * states [n][T / every][d_k][d_v], checkpoint i holding S after token
+ * every * (i + 1).
  */
 #include <math.h>
 #include <pthread.h>
@@ -42,7 +47,7 @@ void kda_oracle_gate(const double* a, double* g, int64_t n) {
 /* One sequence, T tokens, eq. (1) applied token by token. */
 static void kda_oracle_sequence(int T, int dk, int dv, const double* q, const double* k, const double* v,
                                 const double* gate, int gate_is_logit, const double* beta, const double* s0,
-                                double* o, double* S, double* alpha, double* e) {
+                                double* o, double* S, double* alpha, double* e, double* states, int every) {
   if (s0) {
     memcpy(S, s0, sizeof(double) * (size_t)dk * dv);
   } else {
@@ -76,13 +81,17 @@ static void kda_oracle_sequence(int T, int dk, int dv, const double* q, const do
     for (int j = 0; j < dv; ++j) ot[j] = 0.0;
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j) ot[j] += qt[i] * S[(size_t)i * dv + j];
+
+    /* checkpoint: the state after token t + 1 of the sequence */
+    if (states && (t + 1) % every == 0)
+      memcpy(states + (size_t)((t + 1) / every - 1) * dk * dv, S, sizeof(double) * (size_t)dk * dv);
   }
 }
 
 typedef struct {
-  int first, last, T, dk, dv, gate_is_logit;
+  int first, last, T, dk, dv, gate_is_logit, every;
   const double *q, *k, *v, *gate, *beta, *s0;
-  double *o, *s_final;
+  double *o, *s_final, *states;
   int failed;
 } kda_oracle_job;
 
@@ -97,10 +106,12 @@ static void* kda_oracle_worker(void* arg) {
     return NULL;
   }
   size_t T = (size_t)j->T, dk = (size_t)j->dk, dv = (size_t)j->dv;
+  size_t per_seq = j->states ? (T / (size_t)j->every) * dk * dv : 0;
   for (int n = j->first; n < j->last; ++n) {
     kda_oracle_sequence(j->T, j->dk, j->dv, j->q + n * T * dk, j->k + n * T * dk, j->v + n * T * dv,
                         j->gate + n * T * dk, j->gate_is_logit, j->beta + n * T, j->s0 ? j->s0 + n * dk * dv : NULL,
-                        j->o + n * T * dv, j->s_final + n * dk * dv, alpha, e);
+                        j->o + n * T * dv, j->s_final + n * dk * dv, alpha, e,
+                        j->states ? j->states + n * per_seq : NULL, j->every);
   }
   free(alpha);
   free(e);
@@ -110,12 +121,15 @@ static void* kda_oracle_worker(void* arg) {
 /*
  * n_units independent sequences, each of T tokens.  gate holds log-decays g
  * (gate_is_logit = 0) or gate logits a (gate_is_logit = 1, g = -5 sigmoid(a)).
- * Returns 0 on success, -1 on bad arguments, -2 if memory ran out.
+ * states, when not NULL, receives the checkpoints every `every` tokens
+ * [n_units][T / every][dk][dv].  Returns 0 on success, -1 on bad arguments,
+ * -2 if memory ran out.
  */
-int kda_oracle_forward(int n_units, int T, int dk, int dv, const double* q, const double* k, const double* v,
-                       const double* gate, int gate_is_logit, const double* beta, const double* s0, double* o,
-                       double* s_final, int n_threads) {
+int kda_oracle_forward_states(int n_units, int T, int dk, int dv, const double* q, const double* k, const double* v,
+                              const double* gate, int gate_is_logit, const double* beta, const double* s0, double* o,
+                              double* s_final, double* states, int every, int n_threads) {
   if (n_units < 0 || T < 0 || dk <= 0 || dv <= 0 || !s_final) return -1;
+  if (states && every <= 0) return -1;
   if (T > 0 && (!q || !k || !v || !gate || !beta || !o)) return -1;
   if (n_threads < 1) n_threads = 1;
   if (n_threads > 256) n_threads = 256;
@@ -124,7 +138,7 @@ int kda_oracle_forward(int n_units, int T, int dk, int dv, const double* q, cons
   kda_oracle_job jobs[256];
   for (int i = 0; i < n_threads; ++i) {
     kda_oracle_job j = {(int)((int64_t)n_units * i / n_threads), (int)((int64_t)n_units * (i + 1) / n_threads),
-                        T, dk, dv, gate_is_logit, q, k, v, gate, beta, s0, o, s_final, 0};
+                        T, dk, dv, gate_is_logit, every, q, k, v, gate, beta, s0, o, s_final, states, 0};
     jobs[i] = j;
   }
   int started = 0;
@@ -138,4 +152,12 @@ int kda_oracle_forward(int n_units, int T, int dk, int dv, const double* q, cons
   for (int i = 0; i < n_threads; ++i)
     if (jobs[i].failed) return -2;
   return 0;
+}
+
+/* kda_oracle_forward_states without checkpoints. */
+int kda_oracle_forward(int n_units, int T, int dk, int dv, const double* q, const double* k, const double* v,
+                       const double* gate, int gate_is_logit, const double* beta, const double* s0, double* o,
+                       double* s_final, int n_threads) {
+  return kda_oracle_forward_states(n_units, T, dk, dv, q, k, v, gate, gate_is_logit, beta, s0, o, s_final, NULL, 0,
+                                   n_threads);
 }

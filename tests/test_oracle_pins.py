@@ -129,6 +129,49 @@ def test_decode_multi_uncommitted_tokens_change_nothing_committed():
     assert not np.allclose(o2[:, 3:], o[:, 3:])
 
 
+def test_checkpoints_beta_zero_closed_form():
+    """beta = 0 leaves only the decay in eq. (1): the state after t tokens is
+    Diag(exp(sum of g over tokens 1..t)) S0, computed here directly, at every
+    checkpoint."""
+    rng = np.random.default_rng(31)
+    B, T, H, d, every = 2, 37, 2, 5, 6
+    q, k, v = (rng.standard_normal((B, T, H, d)) for _ in range(3))
+    g = -5.0 * rng.random((B, T, H, d))
+    s0 = rng.standard_normal((B, H, d, d))
+    _, S, ck = oracle.forward(q, k, v, np.zeros((B, T, H)), g=g, s0=s0, state_every=every)
+    assert ck.shape == (B, H, T // every, d, d)
+    for i in range(T // every):
+        t = every * (i + 1)
+        decay = np.exp(g[:, :t].sum(axis=1))  # [B, H, d]
+        assert np.allclose(ck[:, :, i], decay[..., None] * s0, rtol=1e-12, atol=1e-14)
+    assert np.allclose(S, np.exp(g.sum(axis=1))[..., None] * s0, rtol=1e-12, atol=1e-14)
+
+
+def test_checkpoints_are_the_states_of_each_prefix():
+    """Checkpoint i is the state a run over the first E (i + 1) tokens ends
+    with, bit for bit, and a run resumed from checkpoint i over the remaining
+    tokens reproduces the full run's outputs and final state."""
+    rng = np.random.default_rng(32)
+    B, T, H, d, every = 2, 50, 3, 6, 16
+    q, k, v, a = (rng.standard_normal((B, T, H, d)) for _ in range(4))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = rng.random((B, T, H))
+    s0 = rng.standard_normal((B, H, d, d))
+    o, S, ck = oracle.forward(q, k, v, beta, a=a, s0=s0, state_every=every)
+    o2, S2 = oracle.forward(q, k, v, beta, a=a, s0=s0)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    assert ck.shape == (B, H, 3, d, d)
+    for i in range(3):
+        t = every * (i + 1)
+        _, St = oracle.forward(q[:, :t], k[:, :t], v[:, :t], beta[:, :t], a=a[:, :t], s0=s0)
+        assert np.array_equal(ck[:, :, i], St)
+        o_rest, S_rest = oracle.forward(q[:, t:], k[:, t:], v[:, t:], beta[:, t:], a=a[:, t:], s0=ck[:, :, i])
+        assert np.array_equal(o_rest, o[:, t:]) and np.array_equal(S_rest, S)
+    # fewer tokens than the interval: no checkpoints
+    assert oracle.forward(q[:, :10], k[:, :10], v[:, :10], beta[:, :10], a=a[:, :10], s0=s0,
+                          state_every=every)[2].shape == (B, H, 0, d, d)
+
+
 def test_empty_sequence_returns_initial_state():
     rng = np.random.default_rng(14)
     s0 = rng.standard_normal((2, 4, 4))
