@@ -6,6 +6,8 @@ is no fallback: if libkda.so is missing or was not built, every call raises.
 
     kda_chunk_fwd(q, k, v, a, beta, initial_state=None, o=None, final_state=None)
         -> (o, final_state)
+    kda_chunk_fwd_states(q, k, v, a, beta, state_every, ...) -> (o, final_state, states)
+        (also the state after every state_every tokens)
     kda_decode_step(q, k, v, a, beta, state, o=None) -> o      (state updated in place)
     kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None) -> o
         (K tokens per sequence; the state keeps the first n_commit[b] of them)
@@ -46,6 +48,8 @@ def lib():
         L.kda_chunk_fwd.restype = i
         L.kda_decode_step.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
         L.kda_decode_step.restype = i
+        L.kda_chunk_fwd_states.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd_states.restype = i
         L.kda_decode_multi.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, p]
         L.kda_decode_multi.restype = i
         L.kda_status_string.argtypes = [i]
@@ -131,6 +135,47 @@ def kda_chunk_fwd(q, k, v, a, beta, initial_state=None, o=None, final_state=None
     return o, final_state
 
 
+def kda_chunk_fwd_states(q, k, v, a, beta, state_every, initial_state=None, o=None, final_state=None, states=None,
+                         stream=None):
+    """kda_chunk_fwd that also returns the state after every `state_every`
+    tokens (kda_chunk_fwd_states of include/kda.h): states [B, H, T //
+    state_every, 128, 128] float32.  Returns (o, final_state, states)."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
+    B, T, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _require(q, "q", (B, T, H, Dk), dt, dev)
+    _require(k, "k", (B, T, H, Dk), dt, dev)
+    _require(a, "a", (B, T, H, Dk), dt, dev)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, T, H, Dv]")
+    Dv = v.shape[3]
+    _require(v, "v", (B, T, H, Dv), dt, dev)
+    _require(beta, "beta", (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (B, H, Dk, Dv), torch.float32, dev)
+    every = int(state_every)
+    if every <= 0 or every % 16:
+        raise ValueError(f"state_every must be a positive multiple of 16, got {state_every}")
+    n = T // every
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    _require(o, "o", (B, T, H, Dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", (B, H, Dk, Dv), torch.float32, dev)
+    if states is None:
+        states = torch.empty((B, H, n, Dk, Dv), dtype=torch.float32, device=dev)
+    _require(states, "states", (B, H, n, Dk, Dv), torch.float32, dev)
+    _check(lib().kda_chunk_fwd_states(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                      _ptr(final_state), _ptr(states) if n > 0 else None, every, B, T, H, Dk, Dv, code,
+                                      _stream(dev, stream)))
+    return o, final_state, states
+
+
 def kda_decode_step(q, k, v, a, beta, state, o=None, stream=None):
     """One recurrent step (kda_decode_step of include/kda.h); state is
     updated in place.  Returns o."""
@@ -193,6 +238,12 @@ def raw_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, 
     """Direct call of the C entry point with raw integer pointers; returns
     the status code without raising (used by the error-path tests)."""
     return lib().kda_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, stream)
+
+
+def raw_chunk_fwd_states(q, k, v, a, beta, initial_state, o, final_state, states, state_every, B, T, H, Dk, Dv, dtype,
+                         stream=0):
+    return lib().kda_chunk_fwd_states(q, k, v, a, beta, initial_state, o, final_state, states, state_every, B, T, H,
+                                      Dk, Dv, dtype, stream)
 
 
 def raw_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream=0):

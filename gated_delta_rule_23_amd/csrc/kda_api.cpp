@@ -82,12 +82,11 @@ hipError_t device_cu_count(hipStream_t stream, int* cus) {
 
 }  // namespace kda
 
-extern "C" {
+namespace {
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
-                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
-                         int Dv, kda_dtype dtype, void* hip_stream) {
-  static const char* fn = "kda_chunk_fwd";
+kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* a,
+                          const float* beta, const float* initial_state, void* o, float* final_state, float* states,
+                          int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
   KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
   if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
   const int64_t units = (int64_t)B * H;
@@ -108,10 +107,34 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
     KDA_TRY(check_ptr(fn, "beta", beta));
     KDA_TRY(check_ptr(fn, "o", o));
   }
+  if (states || state_every) {
+    if (state_every <= 0 || state_every % 16 != 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_every=%d must be a positive multiple of 16", fn, state_every);
+    if (T / state_every > 0) KDA_TRY(check_ptr(fn, "states", states));
+  }
   hipError_t e = kda::launch_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, dtype == KDA_BF16,
-                                       static_cast<hipStream_t>(hip_stream));
+                                       static_cast<hipStream_t>(hip_stream), states, state_every);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                         int Dv, kda_dtype dtype, void* hip_stream) {
+  return chunk_fwd_impl("kda_chunk_fwd", q, k, v, a, beta, initial_state, o, final_state, nullptr, 0, B, T, H, Dk,
+                        Dv, dtype, hip_stream);
+}
+
+kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                const float* initial_state, void* o, float* final_state, float* states,
+                                int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                                void* hip_stream) {
+  return chunk_fwd_impl("kda_chunk_fwd_states", q, k, v, a, beta, initial_state, o, final_state, states,
+                        state_every, B, T, H, Dk, Dv, dtype, hip_stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,

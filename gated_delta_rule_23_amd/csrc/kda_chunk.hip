@@ -81,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
                                                              const IO* __restrict__ v, const IO* __restrict__ a,
                                                              const float* __restrict__ beta,
                                                              const float* initial_state, IO* __restrict__ o,
-                                                             float* final_state, int T, int H) {
+                                                             float* final_state, int T, int H,
+                                                             float* states, int state_every, int n_states) {
   __shared__ Smem<OT> sm;
   const int unit = blockIdx.x;  // b * H + h
   const int bb = unit / H, hh = unit % H;
@@ -275,6 +276,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       const rsrc_t ro = make_rsrc(o_seq + rows_next - 4 * rows_step, rows_bytes(x));
 #pragma unroll
       for (int j = 0; j < 4; ++j) Raw<IO>::store(ro, off_row[j], pq[j] + da[j]);
+      // checkpoint: the state after token 16 (x + 1), when that is a multiple of the interval
+      if (states && (x + 1) % state_every == 0 && (x + 1) / state_every <= n_states) {
+        float* dst = states + ((size_t)unit * n_states + (x + 1) / state_every - 1) * kD * kD;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[(size_t)(16 * rt + 4 * h + j) * kD + col] = sacc[rt][j];
+      }
     }
 
     // ------------------------------------------------ solve(i - 2): one wave
@@ -363,15 +372,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                            bool bf16_io, hipStream_t stream) {
+                            bool bf16_io, hipStream_t stream, float* states, int state_every) {
   const int units = B * H;
   if (units == 0) return hipSuccess;
+  // the interval in chunks and the number of checkpoints (none: no checkpoint output)
+  const int every_chunks = states ? state_every / kChunk : 0;
+  const int n_states = states ? T / state_every : 0;
+  if (n_states == 0) states = nullptr;
   if (bf16_io) {
-    return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream);
+    return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream, states,
+                                 every_chunks, n_states);
   } else {
     hipLaunchKernelGGL((chunk_fwd_kernel<float, float>), dim3(units), dim3(kThreads), 0, stream, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state,
-                       T, H);
+                       T, H, states, every_chunks, n_states);
   }
   return hipGetLastError();
 }

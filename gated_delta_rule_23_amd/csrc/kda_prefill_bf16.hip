@@ -133,7 +133,8 @@ __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int
                : "memory", "m0");
 }
 
-template <int kCT>
+// kEmit: also write the state checkpoints (every state_every chunks, n_states of them per sequence).
+template <int kCT, bool kEmit>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
                                                                   const bf16* __restrict__ v,
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
                                                                   const float* __restrict__ beta,
                                                                   const float* initial_state, bf16* __restrict__ o,
                                                                   float* final_state, int T, int H, int unit0,
-                                                                  int unit_end) {
+                                                                  int unit_end, float* states, int state_every,
+                                                                  int n_states) {
   static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
   __shared__ Smem sm;
   __shared__ InQKA s_qka[3];
@@ -396,6 +398,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
       }
     };
+    // The state after chunk x (token 16 (x + 1)) into checkpoint (x + 1) / state_every - 1.
+    auto emit_state = [&](int x) {
+      float* dst = states + ((size_t)unit * n_states + (x + 1) / state_every - 1) * kD * kD;
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[(size_t)(16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n] = sacc[ct][rt][j];
+    };
     // O of chunk x from the LDS tile to o, 16 bytes a lane, every store
     // instruction writing whole rows.  One state tile per chain wave: chain
     // wave 0 (no Gram or solve) stores this workgroup's 128-byte half of all 16
@@ -441,6 +453,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
       if constexpr (kLoadsOnChain) load_v(i, all);
       if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
+      if constexpr (kEmit)
+        if ((kAll || (i >= 4 && i - 4 < nchunks)) && (i - 3) % state_every == 0 && (i - 3) / state_every <= n_states)
+          emit_state(i - 4);
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 0) gram(i - 1, std::true_type(), std::false_type());
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1) gram(i - 1, std::false_type(), std::true_type());
       if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 2) solve(i - 2);
@@ -590,23 +605,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                  const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, float* states, int state_every, int n_states) {
   const int units = B * H;
   if (units == 0) return hipSuccess;
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
   auto launch = [&](bool pairs, int u0, int u1) {
-    if (pairs) {
-      const unsigned grid = (unsigned)(16 * (((int64_t)(u1 - u0) + 7) / 8));
-      hipLaunchKernelGGL(chunk_fwd_bf16_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
-                         H, u0, u1);
-    } else {
-      hipLaunchKernelGGL(chunk_fwd_bf16_kernel<2>, dim3((unsigned)(u1 - u0)), dim3(kThreads), 0, stream,
-                         (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state,
-                         (bf16*)o, final_state, T, H, u0, u1);
-    }
+    const unsigned grid = pairs ? (unsigned)(16 * (((int64_t)(u1 - u0) + 7) / 8)) : (unsigned)(u1 - u0);
+    auto kernel = pairs ? (states ? chunk_fwd_bf16_kernel<1, true> : chunk_fwd_bf16_kernel<1, false>)
+                        : (states ? chunk_fwd_bf16_kernel<2, true> : chunk_fwd_bf16_kernel<2, false>);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                       (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T, H, u0, u1, states, state_every,
+                       n_states);
   };
   // Sequences that fit on the device at once as two workgroups each (one per
   // compute unit, whole groups of 8).

@@ -80,6 +80,29 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          int Dv, kda_dtype dtype, void* hip_stream);
 
 /*
+ * kda_chunk_fwd that also writes state checkpoints: the state after tokens
+ * E, 2E, ..., n E of every sequence, n = floor(T / E), for E = state_every, a
+ * positive multiple of 16 (the chunk).  These are the sparse KDA state
+ * checkpoints of the page "Kimi K3：从三条信息流到完整系统", section
+ * "hybrid prefix cache" (saved at hash-block or turn boundaries so that a
+ * cached prefix can resume from them); the notebook "Kimi K3: Two point eight
+ * trillion parameters, open weights, and forty-seven pages of how" describes
+ * the same in its section "The machine underneath".
+ *
+ *   states   [B, H, n, Dk, Dv] fp32 (written; may be NULL when n = 0)
+ *
+ * Every other argument, and o and final_state, are as in kda_chunk_fwd, with
+ * the same results.  Resuming from checkpoint i (as initial_state) over
+ * tokens E (i + 1) .. T - 1 gives the rest of the outputs and the same final
+ * state (up to rounding).  state_every <= 0 or not a multiple of 16 returns
+ * KDA_ERR_INVALID_ARGUMENT.
+ */
+kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                const float* initial_state, void* o, float* final_state, float* states,
+                                int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                                void* hip_stream);
+
+/*
  * One recurrent decode step: eq. (1) applied to a single token of each of B
  * sequences and H heads, updating the state in place (read once, written
  * once).

@@ -27,8 +27,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_decode_multi", "kda_status_string", "kda_last_error",
-              "kda_version"):
+    for n in ("kda_chunk_fwd", "kda_chunk_fwd_states", "kda_decode_step", "kda_decode_multi", "kda_status_string",
+              "kda_last_error", "kda_version"):
         assert n in names
 
 
@@ -62,6 +62,31 @@ def decode(**kw):
     args = dict(q=P, k=P, v=P, a=P, beta=P, state=P, o=P, B=1, H=1, Dk=128, Dv=128, dtype=kda.KDA_BF16)
     args.update(kw)
     return kda.raw_decode_step(*args.values())
+
+
+def chunk_states(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, initial_state=None, o=P, final_state=P, states=P, state_every=32, B=1,
+                T=64, H=1, Dk=128, Dv=128, dtype=kda.KDA_BF16)
+    args.update(kw)
+    return kda.raw_chunk_fwd_states(*args.values())
+
+
+@pytest.mark.parametrize("every", [0, -16, 8, 24, 100])
+def test_checkpoint_interval_must_be_a_positive_multiple_of_16(lib, every):
+    assert chunk_states(state_every=every) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "state_every" in kda.last_error()
+
+
+def test_checkpoint_buffer_checks(lib):
+    assert chunk_states(states=None) == kda.KDA_ERR_INVALID_ARGUMENT  # T / every = 2 checkpoints to write
+    assert "states" in kda.last_error()
+    assert chunk_states(states=MIS) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "aligned" in kda.last_error()
+    # the checks shared with kda_chunk_fwd run first
+    assert chunk_states(q=None) == kda.KDA_ERR_INVALID_ARGUMENT and "q is NULL" in kda.last_error()
+    assert chunk_states(Dk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.raw_chunk_fwd_states(None, None, None, None, None, None, None, None, None, 16, 0, 16, 4, 128, 128,
+                                    0) == kda.KDA_OK
 
 
 def multi(**kw):
@@ -192,13 +217,17 @@ def _multi_args(torch, dtype):
                 beta=torch.zeros(B, K, H), state=torch.zeros(B, H, D, D))
 
 
-@pytest.mark.parametrize("entry", ["decode", "chunk", "multi"])
+@pytest.mark.parametrize("entry", ["decode", "chunk", "multi", "states"])
 def test_binding_rejects_host_tensors_before_any_call(lib, entry):
     """Host (CPU) tensors never reach the C ABI: their addresses are not
     device pointers.  Every tensor argument is checked, q included."""
     torch = pytest.importorskip("torch")
-    args = {"decode": _decode_args, "chunk": _chunk_args, "multi": _multi_args}[entry](torch, torch.float32)
-    fn = {"decode": kda.kda_decode_step, "chunk": kda.kda_chunk_fwd, "multi": kda.kda_decode_multi}[entry]
+    args = {"decode": _decode_args, "chunk": _chunk_args, "multi": _multi_args,
+            "states": _chunk_args}[entry](torch, torch.float32)
+    if entry == "states":
+        args["state_every"] = 16
+    fn = {"decode": kda.kda_decode_step, "chunk": kda.kda_chunk_fwd, "multi": kda.kda_decode_multi,
+          "states": kda.kda_chunk_fwd_states}[entry]
     with pytest.raises(ValueError, match="q must be a GPU tensor"):
         fn(**args)
 

@@ -362,6 +362,84 @@ def test_decode_empty_batch_is_a_no_op(kda):
     assert o.shape == (0, 4, 128)
 
 
+# --------------------------------------------------------------------------- state checkpoints
+
+
+def _checkpoint_oracle(w, B, T, H, every):
+    h = host_inputs(w, nb=B, nt=T, nh=H)
+    s0 = None if h["s0"] is None else h["s0"].astype(np.float64)
+    return oracle.forward(synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]),
+                          h["beta"].astype(np.float64), a=synth.to_f64(h["a"]), s0=s0, state_every=every)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,every", [(100, 16), (100, 48), (96, 32), (40, 64)])
+def test_checkpoints_against_oracle(kda, dtype, T, every):
+    """The state after every `every` tokens against the oracle's checkpoints,
+    for ragged and whole lengths (T = 96, every = 32: the last checkpoint is
+    the final state; T = 40, every = 64: none); o and the final state are
+    those of kda_chunk_fwd, bit for bit."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=100 + T + every, dtype=dtype)
+    B, H = 2, 3
+    print_case(f"case checkpoints {dtype} B={B} T={T} H={H} every={every}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, S, ck = kda.kda_chunk_fwd_states(x["q"], x["k"], x["v"], x["a"], x["beta"], every, initial_state=x["s0"])
+    o1, S1 = run_prefill(kda, x, x["s0"])
+    assert torch.equal(o, o1) and torch.equal(S, S1)
+    n = T // every
+    assert ck.shape == (B, H, n, 128, 128)
+    if n == 0:
+        return
+    _, _, ck_ref = _checkpoint_oracle(w, B, T, H, every)
+    e = rel_l2(to_np(ck), ck_ref)
+    print_case(f"  rel_l2 checkpoints={e:.3e}")
+    assert e <= TOL[dtype]
+    if T % every == 0:
+        assert torch.equal(ck[:, :, -1], S)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_checkpoints_in_every_launch_layout(kda, dtype):
+    """3 x 97 = 291 sequences on a 256-CU device: 256 as one workgroup each,
+    then 35 as workgroup pairs (two launches), so both prefill layouts write
+    checkpoints; every sequence's checkpoints are checked on their own."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=140, dtype=dtype)
+    B, T, H, every = 3, 80, 97, 32
+    print_case(f"case checkpoints layouts {dtype} B={B} T={T} H={H} every={every}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    _, _, ck = kda.kda_chunk_fwd_states(x["q"], x["k"], x["v"], x["a"], x["beta"], every, initial_state=x["s0"])
+    torch.cuda.synchronize()
+    _, _, ck_ref = _checkpoint_oracle(w, B, T, H, every)
+    c = to_np(ck)
+    num = np.sqrt(((c - ck_ref) ** 2).sum(axis=(3, 4)))
+    den = np.sqrt((ck_ref ** 2).sum(axis=(3, 4)))
+    worst = float((num / den).max())
+    print_case(f"  worst per-checkpoint rel_l2={worst:.3e}")
+    assert worst <= TOL[dtype]
+
+
+def test_resume_from_a_checkpoint(kda):
+    """The prefix-cache use: a run resumed from checkpoint i over the rest of
+    the tokens gives the full run's later outputs and final state."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=141, dtype="bf16")
+    B, T, H, every = 1, 160, 4, 64
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, S, ck = kda.kda_chunk_fwd_states(x["q"], x["k"], x["v"], x["a"], x["beta"], every, initial_state=x["s0"])
+    for i in range(T // every):
+        t = every * (i + 1)
+        rest = {n: x[n][:, t:].contiguous() for n in ("q", "k", "v", "a", "beta")}
+        o2, S2 = kda.kda_chunk_fwd(rest["q"], rest["k"], rest["v"], rest["a"], rest["beta"],
+                                   initial_state=ck[:, :, i].contiguous())
+        torch.cuda.synchronize()
+        assert rel_l2(to_np(o2), to_np(o[:, t:])) <= 1e-2 and rel_l2(to_np(S2), to_np(S)) <= 1e-2
+
+
 # --------------------------------------------------------------------------- several tokens per state
 
 
