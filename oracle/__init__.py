@@ -21,7 +21,9 @@ for ``decode_multi`` a hand-solved two-token commit, the beta = 0 closed form
 at every commit count, and that tokens past the committed prefix change
 neither the committed state nor earlier outputs; for the state checkpoints
 of ``forward(..., state_every=E)`` the beta = 0 closed form, agreement with
-runs over each prefix, and split runs resumed from a checkpoint).
+runs over each prefix, and split runs resumed from a checkpoint; for
+``forward_varlen`` equal-length packing against the batched layout, empty
+sequences keeping their state, and the clamping of offsets).
 """
 import ctypes
 import os
@@ -166,3 +168,32 @@ def decode_multi(q, k, v, beta, state, a=None, g=None, n_commit=None, threads=No
                         threads=threads, **kw)
         committed[b] = Sb[0]
     return o, committed
+
+
+def forward_varlen(q, k, v, beta, cu_seqlens, a=None, g=None, s0=None, threads=None):
+    """N sequences packed along the token axis: q, k, v, a|g [T, H, D];
+    beta [T, H]; sequence n is tokens cu_seqlens[n] .. cu_seqlens[n+1] - 1,
+    offsets clamped to [0, T] (a decreasing pair is an empty sequence);
+    s0 [N, H, Dk, Dv] or None.  Each sequence is the recurrence of
+    ``forward`` on its own rows.  Returns (o [T, H, Dv], S [N, H, Dk, Dv]);
+    rows outside every sequence are left zero."""
+    if (a is None) == (g is None):
+        raise ValueError("pass exactly one of a (gate logits) or g (log-decay)")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    gv = a if a is not None else g
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    S = np.empty((N, H, dk, dv), dtype=np.float64)
+    for n in range(N):
+        c0 = int(min(max(cu[n], 0), T))
+        c1 = int(min(max(cu[n + 1], c0), T))
+        sl = slice(c0, c1)
+        kw = {"a": np.asarray(gv)[None, sl]} if a is not None else {"g": np.asarray(gv)[None, sl]}
+        on, Sn = forward(np.asarray(q)[None, sl], np.asarray(k)[None, sl], np.asarray(v)[None, sl],
+                         np.asarray(beta)[None, sl], s0=None if s0 is None else np.asarray(s0)[n:n + 1],
+                         threads=threads, **kw)
+        o[sl] = on[0]
+        S[n] = Sn[0]
+    return o, S

@@ -172,6 +172,41 @@ def test_checkpoints_are_the_states_of_each_prefix():
                           state_every=every)[2].shape == (B, H, 0, d, d)
 
 
+def test_varlen_equal_lengths_match_the_batched_layout():
+    """N sequences of one length T packed along the token axis are the
+    batched [N, T, H, D] problem: same outputs and states, bit for bit."""
+    rng = np.random.default_rng(41)
+    N, T, H, d = 3, 11, 2, 5
+    q, k, v, a = (rng.standard_normal((N, T, H, d)) for _ in range(4))
+    beta = rng.random((N, T, H))
+    s0 = rng.standard_normal((N, H, d, d))
+    o_b, S_b = oracle.forward(q, k, v, beta, a=a, s0=s0)
+    cu = np.arange(N + 1) * T
+    o_p, S_p = oracle.forward_varlen(q.reshape(N * T, H, d), k.reshape(N * T, H, d), v.reshape(N * T, H, d),
+                                     beta.reshape(N * T, H), cu, a=a.reshape(N * T, H, d), s0=s0)
+    assert np.array_equal(o_p, o_b.reshape(N * T, H, d)) and np.array_equal(S_p, S_b)
+
+
+def test_varlen_empty_sequences_and_clamped_offsets():
+    """A sequence of length 0 keeps its initial state (zeros without one);
+    offsets outside [0, T] are clamped and a decreasing pair is empty, so the
+    sequences below cover tokens [0, 4), [4, 9), [9, 12) and nothing."""
+    rng = np.random.default_rng(42)
+    T, H, d = 12, 2, 4
+    q, k, v, a = (rng.standard_normal((T, H, d)) for _ in range(4))
+    beta = rng.random((T, H))
+    s0 = rng.standard_normal((4, H, d, d))
+    cu = [-5, 4, 9, 40, 7]
+    o, S = oracle.forward_varlen(q, k, v, beta, cu, a=a, s0=s0)
+    assert np.array_equal(S[3], s0[3])
+    for n, (t0, t1) in enumerate([(0, 4), (4, 9), (9, 12), (12, 12)]):
+        on, Sn = oracle.forward(q[None, t0:t1], k[None, t0:t1], v[None, t0:t1], beta[None, t0:t1],
+                                a=a[None, t0:t1], s0=s0[n:n + 1])
+        assert np.array_equal(S[n], Sn[0]) and np.array_equal(o[t0:t1], on[0])
+    _, Sz = oracle.forward_varlen(q, k, v, beta, [0, 0, 12], a=a)
+    assert np.array_equal(Sz[0], np.zeros((H, d, d)))
+
+
 def test_empty_sequence_returns_initial_state():
     rng = np.random.default_rng(14)
     s0 = rng.standard_normal((2, 4, 4))
