@@ -8,6 +8,8 @@ is no fallback: if libkda.so is missing or was not built, every call raises.
         -> (o, final_state)
     kda_chunk_fwd_states(q, k, v, a, beta, state_every, ...) -> (o, final_state, states)
         (also the state after every state_every tokens)
+    kda_chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, ...) -> (o, final_state)
+        (sequences packed along the token axis, [T, H, 128])
     kda_decode_step(q, k, v, a, beta, state, o=None) -> o      (state updated in place)
     kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None) -> o
         (K tokens per sequence; the state keeps the first n_commit[b] of them)
@@ -48,6 +50,8 @@ def lib():
         L.kda_chunk_fwd.restype = i
         L.kda_decode_step.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
         L.kda_decode_step.restype = i
+        L.kda_chunk_fwd_varlen.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd_varlen.restype = i
         L.kda_chunk_fwd_states.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, p]
         L.kda_chunk_fwd_states.restype = i
         L.kda_decode_multi.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, p]
@@ -176,6 +180,44 @@ def kda_chunk_fwd_states(q, k, v, a, beta, state_every, initial_state=None, o=No
     return o, final_state, states
 
 
+def kda_chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, initial_state=None, o=None, final_state=None, stream=None):
+    """Prefill over N sequences packed along the token axis
+    (kda_chunk_fwd_varlen of include/kda.h): q, k, v, a [T, H, 128]; beta
+    [T, H]; cu_seqlens an int32 GPU tensor [N + 1]; states [N, H, 128, 128].
+    Returns (o [T, H, 128], final_state)."""
+    import torch
+
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, 128]")
+    T, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _require(q, "q", (T, H, Dk), dt, dev)
+    _require(k, "k", (T, H, Dk), dt, dev)
+    _require(a, "a", (T, H, Dk), dt, dev)
+    if v.dim() != 3:
+        raise ValueError("v must be [T, H, Dv]")
+    Dv = v.shape[2]
+    _require(v, "v", (T, H, Dv), dt, dev)
+    _require(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+    N = cu_seqlens.shape[0] - 1
+    _require(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=dt, device=dev)
+    _require(o, "o", (T, H, Dv), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    _check(lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(cu_seqlens),
+                                      _ptr(initial_state), _ptr(o), _ptr(final_state), N, T, H, Dk, Dv, code,
+                                      _stream(dev, stream)))
+    return o, final_state
+
+
 def kda_decode_step(q, k, v, a, beta, state, o=None, stream=None):
     """One recurrent step (kda_decode_step of include/kda.h); state is
     updated in place.  Returns o."""
@@ -244,6 +286,12 @@ def raw_chunk_fwd_states(q, k, v, a, beta, initial_state, o, final_state, states
                          stream=0):
     return lib().kda_chunk_fwd_states(q, k, v, a, beta, initial_state, o, final_state, states, state_every, B, T, H,
                                       Dk, Dv, dtype, stream)
+
+
+def raw_chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, initial_state, o, final_state, N, T, H, Dk, Dv, dtype,
+                         stream=0):
+    return lib().kda_chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, initial_state, o, final_state, N, T, H, Dk, Dv,
+                                      dtype, stream)
 
 
 def raw_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream=0):

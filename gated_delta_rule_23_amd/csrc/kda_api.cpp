@@ -86,7 +86,8 @@ namespace {
 
 kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* a,
                           const float* beta, const float* initial_state, void* o, float* final_state, float* states,
-                          int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+                          int state_every, const int* cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                          kda_dtype dtype, void* hip_stream) {
   KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
   if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
   const int64_t units = (int64_t)B * H;
@@ -95,7 +96,8 @@ kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
   if (H > kMaxPrefillHeads)
     return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d exceeds the prefill limit of %d heads", fn, H, kMaxPrefillHeads);
   // every element index (b, t, h, channel) must fit in 63 bits: B*T*H*128 < 2^62
-  if ((double)B * (double)T * (double)H * 128.0 > 4.0e18)
+  // (packed sequences share the T rows: T*H*128)
+  if ((cu_seqlens ? 1.0 : (double)B) * (double)T * (double)H * 128.0 > 4.0e18)
     return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*T*H*128 overflows the index range", fn);
   KDA_TRY(check_ptr(fn, "final_state", final_state));
   if (initial_state) KDA_TRY(check_ptr(fn, "initial_state", initial_state));
@@ -113,7 +115,7 @@ kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
     if (T / state_every > 0) KDA_TRY(check_ptr(fn, "states", states));
   }
   hipError_t e = kda::launch_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, dtype == KDA_BF16,
-                                       static_cast<hipStream_t>(hip_stream), states, state_every);
+                                       static_cast<hipStream_t>(hip_stream), states, state_every, cu_seqlens);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -125,8 +127,8 @@ extern "C" {
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                          const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
                          int Dv, kda_dtype dtype, void* hip_stream) {
-  return chunk_fwd_impl("kda_chunk_fwd", q, k, v, a, beta, initial_state, o, final_state, nullptr, 0, B, T, H, Dk,
-                        Dv, dtype, hip_stream);
+  return chunk_fwd_impl("kda_chunk_fwd", q, k, v, a, beta, initial_state, o, final_state, nullptr, 0, nullptr, B, T,
+                        H, Dk, Dv, dtype, hip_stream);
 }
 
 kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, const void* a, const float* beta,
@@ -134,7 +136,18 @@ kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, con
                                 int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
                                 void* hip_stream) {
   return chunk_fwd_impl("kda_chunk_fwd_states", q, k, v, a, beta, initial_state, o, final_state, states,
-                        state_every, B, T, H, Dk, Dv, dtype, hip_stream);
+                        state_every, nullptr, B, T, H, Dk, Dv, dtype, hip_stream);
+}
+
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                const int* cu_seqlens, const float* initial_state, void* o, float* final_state, int N,
+                                int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_chunk_fwd_varlen";
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is not 4-byte aligned", fn);
+  return chunk_fwd_impl(fn, q, k, v, a, beta, initial_state, o, final_state, nullptr, 0, cu_seqlens, N, T, H, Dk, Dv,
+                        dtype, hip_stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,

@@ -81,11 +81,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
                                                              const IO* __restrict__ v, const IO* __restrict__ a,
                                                              const float* __restrict__ beta,
                                                              const float* initial_state, IO* __restrict__ o,
-                                                             float* final_state, int T, int H,
-                                                             float* states, int state_every, int n_states) {
+                                                             float* final_state, int T_all, int H,
+                                                             float* states, int state_every, int n_states,
+                                                             const int* cu_seqlens) {
   __shared__ Smem<OT> sm;
   const int unit = blockIdx.x;  // b * H + h
   const int bb = unit / H, hh = unit % H;
+  // The sequence's first token and length: b T_all and T_all, or, for packed
+  // sequences, cu_seqlens[b] .. cu_seqlens[b + 1] clamped to [0, T_all] (so
+  // any contents of cu_seqlens keep every access inside the tensors).
+  int64_t tok0 = (int64_t)bb * T_all;
+  int T = T_all;
+  if (cu_seqlens) {
+    const int c0 = min(max(cu_seqlens[bb], 0), T_all);
+    const int c1 = min(max(cu_seqlens[bb + 1], c0), T_all);
+    tok0 = c0;
+    T = c1 - c0;
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, h = lane >> 4;
@@ -94,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
 
   // This (b, h) sequence: rows of token t start at seq + t * H * 128.
   const int64_t tok_elems = (int64_t)H * kD;
-  const int64_t seq_off = ((int64_t)bb * T * H + hh) * kD;
-  const float* beta_seq = beta + (int64_t)bb * T * H + hh;
+  const int64_t seq_off = (tok0 * H + hh) * kD;
+  const float* beta_seq = beta + tok0 * H + hh;
   // Byte offsets of this lane's four tokens (4h .. 4h+3) inside a chunk.
   int off_row[4], off_beta[4];
 #pragma unroll
@@ -372,7 +384,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                            bool bf16_io, hipStream_t stream, float* states, int state_every) {
+                            bool bf16_io, hipStream_t stream, float* states, int state_every,
+                            const int* cu_seqlens) {
   const int units = B * H;
   if (units == 0) return hipSuccess;
   // the interval in chunks and the number of checkpoints (none: no checkpoint output)
@@ -381,11 +394,11 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
   if (n_states == 0) states = nullptr;
   if (bf16_io) {
     return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream, states,
-                                 every_chunks, n_states);
+                                 every_chunks, n_states, cu_seqlens);
   } else {
     hipLaunchKernelGGL((chunk_fwd_kernel<float, float>), dim3(units), dim3(kThreads), 0, stream, (const float*)q,
                        (const float*)k, (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state,
-                       T, H, states, every_chunks, n_states);
+                       T, H, states, every_chunks, n_states, cu_seqlens);
   }
   return hipGetLastError();
 }

@@ -25,14 +25,18 @@ hipError_t launch_decode_multi(const void* q, const void* k, const void* v, cons
 
 /* Chunkwise prefill over [B, T, H, 128] rows: fp32 or bf16 I/O (kda_chunk.hip).
  * states: NULL, or [B, H, T / state_every, 128, 128] checkpoints, the state
- * after every state_every tokens (a multiple of 16). */
+ * after every state_every tokens (a multiple of 16).  cu_seqlens: NULL, or
+ * [B + 1] token offsets of B sequences packed along the T tokens of one row
+ * (then no checkpoints). */
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                            bool bf16_io, hipStream_t stream, float* states = nullptr, int state_every = 0);
+                            bool bf16_io, hipStream_t stream, float* states = nullptr, int state_every = 0,
+                            const int* cu_seqlens = nullptr);
 
 /* The bf16 I/O prefill (kda_prefill_bf16.hip); launch_chunk_fwd dispatches to it. */
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                  const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                                 hipStream_t stream, float* states, int state_every, int n_states);
+                                 hipStream_t stream, float* states, int state_every, int n_states,
+                                 const int* cu_seqlens);
 
 }  // namespace kda

@@ -134,16 +134,17 @@ __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int
 }
 
 // kEmit: also write the state checkpoints (every state_every chunks, n_states of them per sequence).
-template <int kCT, bool kEmit>
+// kVarlen: sequences packed along the token axis, delimited by cu_seqlens.
+template <int kCT, bool kEmit, bool kVarlen>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
                                                                   const bf16* __restrict__ v,
                                                                   const bf16* __restrict__ a,
                                                                   const float* __restrict__ beta,
                                                                   const float* initial_state, bf16* __restrict__ o,
-                                                                  float* final_state, int T, int H, int unit0,
+                                                                  float* final_state, int T_all, int H, int unit0,
                                                                   int unit_end, float* states, int state_every,
-                                                                  int n_states) {
+                                                                  int n_states, const int* cu_seqlens) {
   static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
   __shared__ Smem sm;
   __shared__ InQKA s_qka[3];
@@ -159,6 +160,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   const int half = kCT == 2 ? 0 : (int)((blockIdx.x >> 3) & 1);
   if (unit >= unit_end) return;  // whole workgroup, before any barrier
   const int bb = unit / H, hh = unit % H;
+  // The sequence's first token and length: b T_all and T_all, or, for packed
+  // sequences, cu_seqlens[b] .. cu_seqlens[b + 1] clamped to [0, T_all] (so
+  // any contents of cu_seqlens keep every access inside the tensors).
+  int64_t tok0 = (int64_t)bb * T_all;
+  int T = T_all;
+  if constexpr (kVarlen) {
+    const int c0 = min(max(cu_seqlens[bb], 0), T_all);
+    const int c1 = min(max(cu_seqlens[bb + 1], c0), T_all);
+    tok0 = c0;
+    T = c1 - c0;
+  }
   // The wave index is uniform; saying so keeps everything derived from it
   // (buffer resources, branch conditions) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -172,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   // Token t of this sequence starts tok_bytes * t bytes into its tensor.  A
   // chunk is a buffer resource sized to its valid tokens (loads past T return
   // 0, stores there are dropped; chunks outside [0, nchunks) have size 0).
-  const int64_t seq_off = ((int64_t)bb * T * H + hh) * kD;
+  const int64_t seq_off = (tok0 * H + hh) * kD;
   const int tok_bytes = H * kD * (int)sizeof(bf16);
   const int64_t rows_step = (int64_t)kChunk * tok_bytes;
   const int64_t beta_step = (int64_t)kChunk * H * (int64_t)sizeof(float);
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   constexpr bool kLoadsOnChain = kCT == 1;
   const int ldw = wave & 3;
   const char* ld_seq = reinterpret_cast<const char*>((ldw == 0 ? q : ldw == 1 ? k : ldw == 2 ? a : v) + seq_off);
-  const char* beta_seq = reinterpret_cast<const char*>(beta + (int64_t)bb * T * H + hh);
+  const char* beta_seq = reinterpret_cast<const char*>(beta + tok0 * H + hh);
   const int beta_off = n * H * (int)sizeof(float);
   // full: the chunks are known to be whole, their resources need no range tests
   auto dma_rows = [&](int x, bf16* dst, auto full) {
@@ -605,7 +617,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                  const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                                 hipStream_t stream, float* states, int state_every, int n_states) {
+                                 hipStream_t stream, float* states, int state_every, int n_states,
+                                 const int* cu_seqlens) {
   const int units = B * H;
   if (units == 0) return hipSuccess;
   int cus = 0;
@@ -613,11 +626,14 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
   if (err != hipSuccess) return err;
   auto launch = [&](bool pairs, int u0, int u1) {
     const unsigned grid = pairs ? (unsigned)(16 * (((int64_t)(u1 - u0) + 7) / 8)) : (unsigned)(u1 - u0);
-    auto kernel = pairs ? (states ? chunk_fwd_bf16_kernel<1, true> : chunk_fwd_bf16_kernel<1, false>)
-                        : (states ? chunk_fwd_bf16_kernel<2, true> : chunk_fwd_bf16_kernel<2, false>);
+    // checkpoints and packed sequences are not requested together
+    auto kernel = pairs ? (states ? chunk_fwd_bf16_kernel<1, true, false>
+                                  : cu_seqlens ? chunk_fwd_bf16_kernel<1, false, true> : chunk_fwd_bf16_kernel<1, false, false>)
+                        : (states ? chunk_fwd_bf16_kernel<2, true, false>
+                                  : cu_seqlens ? chunk_fwd_bf16_kernel<2, false, true> : chunk_fwd_bf16_kernel<2, false, false>);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                        (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T, H, u0, u1, states, state_every,
-                       n_states);
+                       n_states, cu_seqlens);
   };
   // Sequences that fit on the device at once as two workgroups each (one per
   // compute unit, whole groups of 8).

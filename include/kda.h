@@ -103,6 +103,32 @@ kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, con
                                 void* hip_stream);
 
 /*
+ * kda_chunk_fwd over N sequences of different lengths packed one after
+ * another along the token axis (the usual layout of a serving batch):
+ * sequence n is tokens cu_seqlens[n] .. cu_seqlens[n + 1] - 1 of the packed
+ * rows, and each (sequence, head) is an independent KDA recurrence exactly
+ * as in kda_chunk_fwd.
+ *
+ *   q, k, a        [T, H, Dk]     dtype   (read; T = cu_seqlens[N], the packed length)
+ *   v              [T, H, Dv]     dtype   (read)
+ *   beta           [T, H]         fp32    (read)
+ *   cu_seqlens     [N + 1]        int32 on the device, 4-byte aligned: 0 = cu_seqlens[0]
+ *                                 <= cu_seqlens[1] <= ... <= cu_seqlens[N] = T
+ *   initial_state  [N, H, Dk, Dv] fp32, or NULL for zeros   (read)
+ *   o              [T, H, Dv]     dtype   (written)
+ *   final_state    [N, H, Dk, Dv] fp32    (written; may be initial_state)
+ *
+ * The library cannot read cu_seqlens on the host; offsets outside [0, T] are
+ * clamped to it and a decreasing pair gives an empty sequence, so no access
+ * leaves the buffers whatever its contents (sequences that overlap leave the
+ * shared rows of o undefined).  A sequence of length 0 copies its initial
+ * state.  The same limits as kda_chunk_fwd apply (H <= 65536).
+ */
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                const int* cu_seqlens, const float* initial_state, void* o, float* final_state, int N,
+                                int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream);
+
+/*
  * One recurrent decode step: eq. (1) applied to a single token of each of B
  * sequences and H heads, updating the state in place (read once, written
  * once).

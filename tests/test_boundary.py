@@ -27,8 +27,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_chunk_fwd", "kda_chunk_fwd_states", "kda_decode_step", "kda_decode_multi", "kda_status_string",
-              "kda_last_error", "kda_version"):
+    for n in ("kda_chunk_fwd", "kda_chunk_fwd_states", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_decode_multi",
+              "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
 
@@ -86,6 +86,26 @@ def test_checkpoint_buffer_checks(lib):
     assert chunk_states(q=None) == kda.KDA_ERR_INVALID_ARGUMENT and "q is NULL" in kda.last_error()
     assert chunk_states(Dk=64) == kda.KDA_ERR_UNSUPPORTED
     assert kda.raw_chunk_fwd_states(None, None, None, None, None, None, None, None, None, 16, 0, 16, 4, 128, 128,
+                                    0) == kda.KDA_OK
+
+
+def varlen(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, cu_seqlens=P, initial_state=None, o=P, final_state=P, N=2, T=64, H=1,
+                Dk=128, Dv=128, dtype=kda.KDA_BF16)
+    args.update(kw)
+    return kda.raw_chunk_fwd_varlen(*args.values())
+
+
+def test_varlen_argument_checks(lib):
+    assert varlen(cu_seqlens=None) == kda.KDA_ERR_INVALID_ARGUMENT and "cu_seqlens" in kda.last_error()
+    assert varlen(cu_seqlens=P + 2) == kda.KDA_ERR_INVALID_ARGUMENT and "aligned" in kda.last_error()
+    assert varlen(q=None) == kda.KDA_ERR_INVALID_ARGUMENT and "q is NULL" in kda.last_error()
+    assert varlen(N=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert varlen(T=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert varlen(Dk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert varlen(H=65537) == kda.KDA_ERR_UNSUPPORTED
+    assert varlen(N=1 << 21, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT  # N*H above the sequence limit
+    assert kda.raw_chunk_fwd_varlen(None, None, None, None, None, P, None, None, None, 0, 0, 4, 128, 128,
                                     0) == kda.KDA_OK
 
 
@@ -217,17 +237,20 @@ def _multi_args(torch, dtype):
                 beta=torch.zeros(B, K, H), state=torch.zeros(B, H, D, D))
 
 
-@pytest.mark.parametrize("entry", ["decode", "chunk", "multi", "states"])
+@pytest.mark.parametrize("entry", ["decode", "chunk", "multi", "states", "varlen"])
 def test_binding_rejects_host_tensors_before_any_call(lib, entry):
     """Host (CPU) tensors never reach the C ABI: their addresses are not
     device pointers.  Every tensor argument is checked, q included."""
     torch = pytest.importorskip("torch")
-    args = {"decode": _decode_args, "chunk": _chunk_args, "multi": _multi_args,
-            "states": _chunk_args}[entry](torch, torch.float32)
+    args = {"decode": _decode_args, "chunk": _chunk_args, "multi": _multi_args, "states": _chunk_args,
+            "varlen": _chunk_args}[entry](torch, torch.float32)
     if entry == "states":
         args["state_every"] = 16
+    if entry == "varlen":
+        args = {n: t[0] for n, t in args.items()}
+        args["cu_seqlens"] = torch.tensor([0, 5], dtype=torch.int32)
     fn = {"decode": kda.kda_decode_step, "chunk": kda.kda_chunk_fwd, "multi": kda.kda_decode_multi,
-          "states": kda.kda_chunk_fwd_states}[entry]
+          "states": kda.kda_chunk_fwd_states, "varlen": kda.kda_chunk_fwd_varlen}[entry]
     with pytest.raises(ValueError, match="q must be a GPU tensor"):
         fn(**args)
 

@@ -440,6 +440,98 @@ def test_resume_from_a_checkpoint(kda):
         assert rel_l2(to_np(o2), to_np(o[:, t:])) <= 1e-2 and rel_l2(to_np(S2), to_np(S)) <= 1e-2
 
 
+# --------------------------------------------------------------------------- packed variable-length sequences
+
+
+def _packed(w, lengths, H, dtype_name):
+    """Sequences of the given lengths drawn as one [1, T, H] workload row,
+    with offsets; plus the host copy for the oracle."""
+    import torch
+
+    T = int(sum(lengths))
+    x = device_inputs(w, B=1, T=T, H=H)
+    h = host_inputs(w, nb=1, nt=T, nh=H)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return x, h, cu, torch.tensor(cu, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_varlen_against_oracle(kda, dtype, with_s0):
+    """Lengths 0, 1, 15, 16, 17, 100 and 300 packed together: every
+    sequence against the oracle's run over its own rows."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=150 + int(with_s0), dtype=dtype)
+    lengths, H = [17, 0, 300, 1, 15, 100, 16], 3
+    N = len(lengths)
+    print_case(f"case varlen {dtype} s0={with_s0} lengths={lengths} H={H}")
+    x, h, cu, cu_d = _packed(w, lengths, H, dtype)
+    rng = np.random.default_rng(7)
+    s0 = rng.standard_normal((N, H, 128, 128)).astype(np.float32) * 0.3 if with_s0 else None
+    s0_d = None if s0 is None else torch.from_numpy(s0).cuda()
+    o, S = kda.kda_chunk_fwd_varlen(x["q"][0], x["k"][0], x["v"][0], x["a"][0], x["beta"][0], cu_d,
+                                    initial_state=s0_d)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward_varlen(synth.to_f64(h["q"][0]), synth.to_f64(h["k"][0]), synth.to_f64(h["v"][0]),
+                                         h["beta"][0].astype(np.float64), cu, a=synth.to_f64(h["a"][0]),
+                                         s0=None if s0 is None else s0.astype(np.float64))
+    on, Sn = to_np(o), to_np(S)
+    for n in range(N):
+        t0, t1 = cu[n], cu[n + 1]
+        es = rel_l2(Sn[n], S_ref[n]) if np.linalg.norm(S_ref[n]) > 0 else float(np.abs(Sn[n]).max())
+        eo = rel_l2(on[t0:t1], o_ref[t0:t1]) if t1 > t0 else 0.0
+        print_case(f"  sequence {n} (length {t1 - t0}): rel_l2 o={eo:.3e} S={es:.3e}")
+        assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_varlen_equal_lengths_match_batched(kda, dtype):
+    """Equal lengths packed are the batched call: identical bits."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=152, dtype=dtype)
+    N, T, H = 3, 50, 4
+    x = device_inputs(w, B=N, T=T, H=H)
+    o_b, S_b = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"])
+    flat = {n: x[n].reshape((N * T,) + tuple(x[n].shape[2:])).contiguous() for n in ("q", "k", "v", "a", "beta")}
+    cu = torch.arange(0, N * T + 1, T, dtype=torch.int32, device="cuda")
+    o_p, S_p = kda.kda_chunk_fwd_varlen(flat["q"], flat["k"], flat["v"], flat["a"], flat["beta"], cu,
+                                        initial_state=x["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_b.reshape(N * T, H, 128)) and torch.equal(S_p, S_b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_varlen_many_sequences_both_layouts(kda, dtype):
+    """97 sequences x 3 heads = 291 (sequence, head) pairs on a 256-CU
+    device: single workgroups, then pairs; random lengths 0..70 with clamped
+    bogus offsets at the end (N + 1 offsets, the last two past T)."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=153, dtype=dtype)
+    rng = np.random.default_rng(9)
+    lengths = rng.integers(0, 71, size=95).tolist()
+    H = 3
+    x, h, cu, _ = _packed(w, lengths, H, dtype)
+    T = int(cu[-1])
+    cu_all = np.concatenate([cu, [T + 50, T + 9]]).astype(np.int32)  # two more sequences, both empty after clamping
+    N = len(cu_all) - 1
+    print_case(f"case varlen many {dtype} N={N} T={T} H={H}")
+    o, S = kda.kda_chunk_fwd_varlen(x["q"][0], x["k"][0], x["v"][0], x["a"][0], x["beta"][0],
+                                    torch.tensor(cu_all, device="cuda"))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward_varlen(synth.to_f64(h["q"][0]), synth.to_f64(h["k"][0]), synth.to_f64(h["v"][0]),
+                                         h["beta"][0].astype(np.float64), cu_all, a=synth.to_f64(h["a"][0]))
+    on, Sn = to_np(o), to_np(S)
+    assert rel_l2(on, o_ref) <= TOL[dtype]
+    for n in range(N):
+        if np.linalg.norm(S_ref[n]) == 0:
+            assert not np.any(Sn[n])
+        else:
+            assert rel_l2(Sn[n], S_ref[n]) <= TOL[dtype], n
+
+
 # --------------------------------------------------------------------------- several tokens per state
 
 
