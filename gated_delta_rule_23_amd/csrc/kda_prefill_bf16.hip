@@ -410,7 +410,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
       }
     };
-    // The state after chunk x (token 16 (x + 1)) into checkpoint (x + 1) / state_every - 1.
+    // The state after chunk x (token 16 (x + 1)) into checkpoint (x + 1) / state_every - 1.  The
+    // chunk count of the next checkpoint is carried from one to the next (no division per chunk).
+    int next_emit = state_every;
+    const int last_emit = state_every * n_states;
     auto emit_state = [&](int x) {
       float* dst = states + ((size_t)unit * n_states + (x + 1) / state_every - 1) * kD * kD;
 #pragma unroll
@@ -466,8 +469,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       if constexpr (kLoadsOnChain) load_v(i, all);
       if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
       if constexpr (kEmit)
-        if ((kAll || (i >= 4 && i - 4 < nchunks)) && (i - 3) % state_every == 0 && (i - 3) / state_every <= n_states)
+        if (i - 3 == next_emit && next_emit <= last_emit) {  // chunk i - 4 ends a checkpoint interval
           emit_state(i - 4);
+          next_emit += state_every;
+        }
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 0) gram(i - 1, std::true_type(), std::false_type());
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1) gram(i - 1, std::false_type(), std::true_type());
       if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 2) solve(i - 2);

@@ -1,6 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (one kda_chunk_fwd over the whole batch, or 64
-kda_decode_step calls over the whole state).  The oracle checks sampled
+benchmark times (one kda_chunk_fwd over the whole batch, 64
+kda_decode_step calls over the whole state, or 16 four-token
+kda_decode_multi calls).  The oracle checks sampled
 (batch, head) sequences: whole sequences for the 8K and 32K workloads and for
 decode; token windows for the 1M-token workload.
 
@@ -127,6 +128,39 @@ def test_decode_full_size_sampled(kda):
         outs.append(torch.stack([o[b, h] for b, h in units]))
     torch.cuda.synchronize()
     o_gpu = to_np(torch.stack(outs, dim=1))  # [units, steps, 128]
+    eo_num = eo_den = es_num = es_den = 0.0
+    for n, (b, h) in enumerate(units):
+        o_ref, S_ref = oracle_block(w, b0=b, nb=1, h0=h, nh=1)
+        eo_num += np.sum((o_gpu[n] - o_ref[0, :, 0]) ** 2)
+        eo_den += np.sum(o_ref ** 2)
+        sg = to_np(state[b, h])
+        es_num += np.sum((sg - S_ref[0, 0]) ** 2)
+        es_den += np.sum(S_ref ** 2)
+    eo, es = math.sqrt(eo_num / eo_den), math.sqrt(es_num / es_den)
+    print_case(f"  rel_l2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_decode_multi_full_size_sampled(kda):
+    """The decode workload's 64 tokens per state in 16 kda_decode_multi calls
+    of four tokens over all 256 x 96 states (the benchmark's configuration),
+    every token committed: sampled states and their outputs against the
+    oracle's 64-step run."""
+    import torch
+
+    w = WORKLOADS[4]
+    B, H, steps, kt = w.B, w.H, w.T, 4
+    units = [(0, 0), (17, 5), (100, 50), (201, 77), (255, 95)]
+    print_case(f"case {w.name} in {steps // kt} four-token calls: sampled (b, h) {units}")
+    x = device_inputs(w)
+    state = x["s0"]
+    outs = []
+    for t in range(0, steps, kt):
+        c = {n: x[n][:, t:t + kt].contiguous() for n in ("q", "k", "v", "a", "beta")}
+        o = kda.kda_decode_multi(c["q"], c["k"], c["v"], c["a"], c["beta"], state)
+        outs.append(torch.stack([o[b, :, h] for b, h in units]))  # [units, kt, 128]
+    torch.cuda.synchronize()
+    o_gpu = to_np(torch.cat(outs, dim=1))  # [units, steps, 128]
     eo_num = eo_den = es_num = es_den = 0.0
     for n, (b, h) in enumerate(units):
         o_ref, S_ref = oracle_block(w, b0=b, nb=1, h0=h, nh=1)
