@@ -12,6 +12,10 @@
  *   before the delta correction, as the reference step in that section fixes.
  *   S has Dk rows (key channels) and Dv columns (value channels).
  *   The learned scale e^A of eq. (5) is folded into a by the caller.
+ *   The family's other rules run through the same entry points: a = -inf
+ *   (sigmoid 0, so alpha = 1) gives the plain delta rule, and one logit per
+ *   token and head repeated over the channels gives a scalar-gated delta
+ *   rule with the same bounded gate.
  *
  * Conventions for every entry point:
  *   - Every pointer is a device pointer (hipMalloc'd or equivalent), row-major,

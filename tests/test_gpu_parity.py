@@ -440,6 +440,49 @@ def test_resume_from_a_checkpoint(kda):
         assert rel_l2(to_np(o2), to_np(o[:, t:])) <= 1e-2 and rel_l2(to_np(S2), to_np(S)) <= 1e-2
 
 
+# --------------------------------------------------------------------------- the gate variants
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant_name", ["delta_rule", "scalar_gate"])
+def test_gate_variants_through_the_logits(kda, dtype, variant_name):
+    """The family's other rules through the same kernels: the delta rule
+    (alpha = 1) is the gate logit a = -inf (sigmoid 0, g = 0), and a scalar
+    gated delta rule is one logit per token and head repeated over the
+    channels.  Prefill, single-token decode and multi-token decode against
+    the oracle's log-decay path (g given directly)."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=160 + (variant_name == "scalar_gate"), dtype=dtype)
+    B, T, H = 2, 70, 3
+    x = device_inputs(w, B=B, T=T, H=H)
+    h = host_inputs(w, nb=B, nt=T, nh=H)
+    if variant_name == "delta_rule":
+        a_dev = torch.full_like(x["a"], float("-inf"))
+        g = np.zeros((B, T, H, 128))
+    else:
+        a_dev = x["a"][..., :1].expand(-1, -1, -1, 128).contiguous()
+        g = oracle.gate(np.repeat(synth.to_f64(h["a"])[..., :1], 128, axis=3))
+    qh, kh, vh = synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"])
+    bh, s0 = h["beta"].astype(np.float64), h["s0"].astype(np.float64)
+    o, S = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], a_dev, x["beta"], initial_state=x["s0"])
+    state = x["s0"].clone()
+    od = kda.kda_decode_step(x["q"][:, 0].contiguous(), x["k"][:, 0].contiguous(), x["v"][:, 0].contiguous(),
+                             a_dev[:, 0].contiguous(), x["beta"][:, 0].contiguous(), state)
+    state_m = x["s0"].clone()
+    om = kda.kda_decode_multi(x["q"][:, :5].contiguous(), x["k"][:, :5].contiguous(), x["v"][:, :5].contiguous(),
+                              a_dev[:, :5].contiguous(), x["beta"][:, :5].contiguous(), state_m)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(qh, kh, vh, bh, g=g, s0=s0)
+    od_ref, Sd_ref = oracle.forward(qh[:, :1], kh[:, :1], vh[:, :1], bh[:, :1], g=g[:, :1], s0=s0)
+    om_ref, Sm_ref = oracle.forward(qh[:, :5], kh[:, :5], vh[:, :5], bh[:, :5], g=g[:, :5], s0=s0)
+    errs = [rel_l2(to_np(o), o_ref), rel_l2(to_np(S), S_ref), rel_l2(to_np(od), od_ref[:, 0]),
+            rel_l2(to_np(state), Sd_ref), rel_l2(to_np(om), om_ref), rel_l2(to_np(state_m), Sm_ref)]
+    print_case(f"  {variant_name} {dtype}: rel_l2 prefill o/S, decode o/S, multi o/S = "
+               + " ".join(f"{e:.2e}" for e in errs))
+    assert max(errs) <= TOL[dtype]
+
+
 # --------------------------------------------------------------------------- packed variable-length sequences
 
 
