@@ -11,6 +11,7 @@ kda_decode_multi (one state read and write per call); `cpu_baseline` is the
 fp64 oracle timed on a bounded sample on the host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--decode-tokens K]
+                    [--workload 1|2|3]   (the other prefill workloads; 1 is the default line)
 """
 import argparse
 import hashlib
@@ -132,13 +133,13 @@ def timed_launches(fn, n, stream):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
-def bench_prefill(steps, warmup):
+def bench_prefill(steps, warmup, workload=1):
     import torch
 
     import gated_delta_rule_23_amd as kda
     from synth.workloads import WORKLOADS, device_inputs
 
-    w = WORKLOADS[1]
+    w = WORKLOADS[workload]
     x = device_inputs(w)
     o = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
     S = torch.empty((w.B, w.H, D, D), dtype=torch.float32, device="cuda")
@@ -156,7 +157,9 @@ def bench_prefill(steps, warmup):
     per_launch = timed_launches(step, steps, stream)
     wall = time.perf_counter() - t0
     tokens = w.B * w.T
-    launch_bytes = w.B * w.T * w.H * BYTES_PER_TOKEN_HEAD_BF16 + w.B * w.H * STATE_BYTES
+    # inputs and o per token-head, the final state written, and the initial state read when there is one
+    launch_bytes = (w.B * w.T * w.H * BYTES_PER_TOKEN_HEAD_BF16
+                    + w.B * w.H * STATE_BYTES * (2 if x["s0"] is not None else 1))
     launch_flops = w.B * w.T * w.H * FLOPS_PER_TOKEN_HEAD
     avg_ms = sum(per_launch) / len(per_launch)
     return dict(workload=w, tokens=tokens, wall=wall, per_launch_ms=per_launch, avg_ms=avg_ms,
@@ -278,6 +281,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3],
+                    help="prefill workload: 1 = B1 H96 T8192 (default), 2 = B4 H96 T32768 with S0, "
+                         "3 = B1 H96 T1048576 mixed decay")
     ap.add_argument("--decode-tokens", type=int, default=4,
                     help="tokens per kda_decode_multi call on the decode workload (1 skips that measurement)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -299,12 +305,12 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
 
-    pre = bench_prefill(args.steps, args.warmup)
+    pre = bench_prefill(args.steps, args.warmup, args.workload)
     w = pre["workload"]
     avg_s = pre["avg_ms"] / 1e3
     wall_per_step = pre["wall"] / args.steps
     achieved = pre["launch_bytes"] / avg_s
-    traffic = measured_traffic(PREFILL_KERNEL)
+    traffic = measured_traffic(PREFILL_KERNEL) if args.workload == 1 else None  # counters taken on workload 1
     result = {
         "metric": METRIC,
         "value": pre["tokens"] / wall_per_step,
