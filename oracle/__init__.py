@@ -23,7 +23,9 @@ neither the committed state nor earlier outputs; for the state checkpoints
 of ``forward(..., state_every=E)`` the beta = 0 closed form, agreement with
 runs over each prefix, and split runs resumed from a checkpoint; for
 ``forward_varlen`` equal-length packing against the batched layout, empty
-sequences keeping their state, and the clamping of offsets).
+sequences keeping their state, and the clamping of offsets; for
+``output_gate_norm`` rows of constant magnitude, scale invariance and the
+gate's limits).
 """
 import ctypes
 import os
@@ -197,3 +199,14 @@ def forward_varlen(q, k, v, beta, cu_seqlens, a=None, g=None, s0=None, threads=N
         o[sl] = on[0]
         S[n] = Sn[0]
     return o, S
+
+
+def output_gate_norm(o, z, eps):
+    """The weight-free part of the K3 page's eq. (6) (section "KDA 是带逐通道遗忘
+    的 delta rule" onward, the output gate): y = sigmoid(z) * RMSNorm(o), the
+    RMSNorm taken head-wise, over the last axis (the value channels of one
+    token and head), with no learned scale: o / sqrt(mean(o^2) + eps).  fp64."""
+    o = np.asarray(o, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + float(eps))
+    return (1.0 / (1.0 + np.exp(-z))) * (o / rms)

@@ -207,6 +207,25 @@ def test_varlen_empty_sequences_and_clamped_offsets():
     assert np.array_equal(Sz[0], np.zeros((H, d, d)))
 
 
+def test_output_gate_norm_closed_forms():
+    """Eq. (6) without W_o and W_g: rows of constant magnitude c normalise to
+    their signs (eps = 0); the result does not change when a row is scaled
+    (eps = 0); z = 0 halves RMSNorm(o) and z -> +inf leaves it."""
+    rng = np.random.default_rng(51)
+    signs = rng.choice([-1.0, 1.0], size=(5, 3, 128))
+    z = rng.standard_normal((5, 3, 128))
+    y = oracle.output_gate_norm(3.5 * signs, z, 0.0)
+    assert np.allclose(y, signs / (1.0 + np.exp(-z)), rtol=1e-14, atol=0)
+    o = rng.standard_normal((4, 2, 128))
+    assert np.allclose(oracle.output_gate_norm(o, z[:4, :2], 0.0), oracle.output_gate_norm(7.25 * o, z[:4, :2], 0.0),
+                       rtol=1e-13, atol=1e-15)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + 1e-6)
+    assert np.allclose(oracle.output_gate_norm(o, np.zeros_like(o), 1e-6), 0.5 * o / rms, rtol=1e-14, atol=0)
+    assert np.allclose(oracle.output_gate_norm(o, np.full_like(o, 800.0), 1e-6), o / rms, rtol=1e-14, atol=0)
+    # a zero row stays zero for eps > 0
+    assert not np.any(oracle.output_gate_norm(np.zeros((1, 128)), np.ones((1, 128)), 1e-6))
+
+
 def test_empty_sequence_returns_initial_state():
     rng = np.random.default_rng(14)
     s0 = rng.standard_normal((2, 4, 4))
