@@ -46,7 +46,8 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "chunk_fwd_bf16_kernel"  # the kernel the bf16 prefill workload runs
 COPY_CALIBRATION_BYTES = 1 << 30  # one device-to-device copy of this many bytes (--calibrate-copy)
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
-                  for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_bf16_tiles.h", "kda_common.h", "kda_decode.hip")]
+                  for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_bf16_tiles.h", "kda_common.h", "kda_decode.hip",
+                            "kda_epilogue.hip")]
 
 
 def strip_comments(text):
@@ -164,6 +165,30 @@ def bench_prefill(steps, warmup, workload=1):
     avg_ms = sum(per_launch) / len(per_launch)
     return dict(workload=w, tokens=tokens, wall=wall, per_launch_ms=per_launch, avg_ms=avg_ms,
                 launch_bytes=launch_bytes, launch_flops=launch_flops)
+
+
+def bench_gate_norm(w, reps=50):
+    """kda_output_gate_norm over a prefill output's B*T*H rows of 128 bf16
+    channels (o and the gate read, y written)."""
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    o = torch.randn((w.B, w.T, w.H, D), device="cuda", generator=g).to(torch.bfloat16)
+    z = torch.randn((w.B, w.T, w.H, D), device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.empty_like(o)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        kda.kda_output_gate_norm(o, z, 1e-6, y=y, stream=stream)
+
+    for _ in range(5):
+        one()
+    torch.cuda.synchronize()
+    ms = timed_launches(one, reps, stream)
+    rows = w.B * w.T * w.H
+    return dict(rows=rows, avg_ms=sum(ms) / len(ms), bytes=3 * rows * D * 2)
 
 
 def bench_decode(reps=3):
@@ -334,6 +359,14 @@ def main():
                  "achieved_tflops": pre["launch_flops"] / avg_s / 1e12,
                  "frac_of_bf16_peak": pre["launch_flops"] / avg_s / BF16_MFMA_PEAK},
     }
+    if args.workload == 1:
+        # the eq. (6) epilogue over the prefill's output rows (o and the gate read, y written once)
+        gn = bench_gate_norm(pre["workload"])
+        result["output_gate_norm"] = {
+            "rows": gn["rows"], "ms_per_launch": gn["avg_ms"], "kernel": "gate_norm_kernel",
+            "hbm": {"achieved": gn["bytes"] / (gn["avg_ms"] / 1e3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                    "frac": gn["bytes"] / (gn["avg_ms"] / 1e3) / HBM_PEAK, "algorithmic_bytes_per_launch": gn["bytes"]},
+        }
     if not args.no_decode:
         torch.cuda.empty_cache()
         dec = bench_decode()

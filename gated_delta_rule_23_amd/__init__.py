@@ -11,6 +11,7 @@ is no fallback: if libkda.so is missing or was not built, every call raises.
     kda_chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, ...) -> (o, final_state)
         (sequences packed along the token axis, [T, H, 128])
     kda_decode_step(q, k, v, a, beta, state, o=None) -> o      (state updated in place)
+    kda_output_gate_norm(o, z, eps=1e-6, y=None) -> y   (sigmoid(z) * RMSNorm(o), eq. (6) without W_o, W_g)
     kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None) -> o
         (K tokens per sequence; the state keeps the first n_commit[b] of them)
 
@@ -56,6 +57,8 @@ def lib():
         L.kda_chunk_fwd_states.restype = i
         L.kda_decode_multi.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, p]
         L.kda_decode_multi.restype = i
+        L.kda_output_gate_norm.argtypes = [p, p, p, ctypes.c_int64, i, ctypes.c_float, i, p]
+        L.kda_output_gate_norm.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -276,6 +279,26 @@ def kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None, stream=None
     return o
 
 
+def kda_output_gate_norm(o, z, eps=1e-6, y=None, stream=None):
+    """y = sigmoid(z) * o / sqrt(mean(o^2) + eps) over the last axis of 128
+    value channels (kda_output_gate_norm of include/kda.h); o and z of one
+    shape and dtype, y may be o.  Returns y."""
+    if o.shape[-1] != D:
+        raise ValueError(f"the last axis of o must have {D} channels")
+    dev, dt = o.device, o.dtype
+    code = _dtype_code(o)
+    _require(o, "o", tuple(o.shape), dt, dev)
+    _require(z, "z", tuple(o.shape), dt, dev)
+    if y is None:
+        import torch
+
+        y = torch.empty_like(o)
+    _require(y, "y", tuple(o.shape), dt, dev)
+    rows = o.numel() // D
+    _check(lib().kda_output_gate_norm(_ptr(o), _ptr(z), _ptr(y), rows, D, float(eps), code, _stream(dev, stream)))
+    return y
+
+
 def raw_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, stream=0):
     """Direct call of the C entry point with raw integer pointers; returns
     the status code without raising (used by the error-path tests)."""
@@ -300,6 +323,10 @@ def raw_decode_step(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, stream=0):
 
 def raw_decode_multi(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype, stream=0):
     return lib().kda_decode_multi(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype, stream)
+
+
+def raw_output_gate_norm(o, z, y, rows, Dv, eps, dtype, stream=0):
+    return lib().kda_output_gate_norm(o, z, y, rows, Dv, eps, dtype, stream)
 
 
 def last_error():

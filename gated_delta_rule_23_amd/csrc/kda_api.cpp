@@ -197,6 +197,24 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
   return ok();
 }
 
+kda_status kda_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, int Dv, float eps,
+                                kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_output_gate_norm";
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+  if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (rows=%lld)", fn, (long long)rows);
+  if (Dv <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: head size must be positive (Dv=%d)", fn, Dv);
+  if (Dv != 128) return fail(KDA_ERR_UNSUPPORTED, "%s: only Dv = 128 is implemented (got Dv=%d)", fn, Dv);
+  if (!(eps >= 0.0f) || eps > 1.0e30f) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (rows > ((int64_t)1 << 40)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: rows=%lld is too large", fn, (long long)rows);
+  if (rows == 0) return ok();
+  KDA_TRY(check_ptr(fn, "o", o));
+  KDA_TRY(check_ptr(fn, "z", z));
+  KDA_TRY(check_ptr(fn, "y", y));
+  hipError_t e = kda::launch_output_gate_norm(o, z, y, rows, eps, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 const char* kda_status_string(kda_status status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";

@@ -33,6 +33,10 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
                             bool bf16_io, hipStream_t stream, float* states = nullptr, int state_every = 0,
                             const int* cu_seqlens = nullptr);
 
+/* y = sigmoid(z) * o / sqrt(mean(o^2) + eps) over rows of 128 channels (kda_epilogue.hip). */
+hipError_t launch_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, float eps, bool bf16_io,
+                                   hipStream_t stream);
+
 /* The bf16 I/O prefill (kda_prefill_bf16.hip); launch_chunk_fwd dispatches to it. */
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                  const float* initial_state, void* o, float* final_state, int B, int T, int H,

@@ -40,6 +40,8 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -182,6 +184,21 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
 kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
                             kda_dtype dtype, void* hip_stream);
+
+/*
+ * The output side of eq. (6) of the page "Kimi K3：从三条信息流到完整系统"
+ * without its two projections: y = sigmoid(z) * o / sqrt(mean(o^2) + eps),
+ * the head-wise RMSNorm (no learned scale) of each row of Dv value channels
+ * of the recurrent output o, gated by z = W_g x computed by the caller.
+ *
+ *   o, z   [rows, Dv]  dtype  (read; rows = B * T * H for a prefill's o)
+ *   y      [rows, Dv]  dtype  (written; may be o itself)
+ *
+ * Dv = 128 only.  eps must be finite and non-negative (a zero row gives zeros
+ * for eps > 0).
+ */
+kda_status kda_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, int Dv, float eps,
+                                kda_dtype dtype, void* hip_stream);
 
 /* Static text for a status code. */
 const char* kda_status_string(kda_status status);

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_chunk_fwd_states", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_decode_multi",
-              "kda_status_string", "kda_last_error", "kda_version"):
+              "kda_output_gate_norm", "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
 
@@ -107,6 +107,23 @@ def test_varlen_argument_checks(lib):
     assert varlen(N=1 << 21, H=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT  # N*H above the sequence limit
     assert kda.raw_chunk_fwd_varlen(None, None, None, None, None, P, None, None, None, 0, 0, 4, 128, 128,
                                     0) == kda.KDA_OK
+
+
+def test_output_gate_norm_argument_checks(lib):
+    def call(**kw):
+        args = dict(o=P, z=P, y=P, rows=8, Dv=128, eps=1e-6, dtype=kda.KDA_BF16)
+        args.update(kw)
+        return kda.raw_output_gate_norm(*args.values())
+
+    for field in ("o", "z", "y"):
+        assert call(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT and field in kda.last_error()
+        assert call(**{field: MIS}) == kda.KDA_ERR_INVALID_ARGUMENT and "aligned" in kda.last_error()
+    assert call(rows=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(Dv=64) == kda.KDA_ERR_UNSUPPORTED
+    assert call(eps=-1.0) == kda.KDA_ERR_INVALID_ARGUMENT and "eps" in kda.last_error()
+    assert call(eps=float("nan")) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(dtype=5) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert kda.raw_output_gate_norm(None, None, None, 0, 128, 1e-6, 0) == kda.KDA_OK
 
 
 def multi(**kw):

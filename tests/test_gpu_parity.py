@@ -483,6 +483,32 @@ def test_gate_variants_through_the_logits(kda, dtype, variant_name):
     assert max(errs) <= TOL[dtype]
 
 
+# --------------------------------------------------------------------------- output gate and norm
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_output_gate_norm_against_oracle(kda, dtype):
+    """sigmoid(z) * RMSNorm(o) on a prefill's own output (an odd number of
+    rows, so one wave has a dead half) and on rows with a zero row, in place
+    and out of place, against the oracle."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=170, dtype=dtype)
+    B, T, H = 1, 37, 3
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, _ = run_prefill(kda, x, x["s0"])
+    z = x["q"] * 2.0  # any gate pre-activation of the same shape
+    o[0, 5, 1] = 0
+    y = kda.kda_output_gate_norm(o, z, 1e-6)
+    o2 = o.clone()
+    kda.kda_output_gate_norm(o2, z, 1e-6, y=o2)
+    torch.cuda.synchronize()
+    ref = oracle.output_gate_norm(to_np(o), to_np(z), 1e-6)
+    e = rel_l2(to_np(y), ref)
+    print_case(f"  output gate norm {dtype}: rel_l2 {e:.3e}")
+    assert e <= TOL[dtype] and torch.equal(y, o2) and not y[0, 5, 1].any()
+
+
 # --------------------------------------------------------------------------- packed variable-length sequences
 
 
