@@ -59,6 +59,8 @@ def lib():
         L.kda_decode_multi.restype = i
         L.kda_output_gate_norm.argtypes = [p, p, p, ctypes.c_int64, i, ctypes.c_float, i, p]
         L.kda_output_gate_norm.restype = i
+        L.kda_compose_segments.argtypes = [p, p, p, p, i, i, i, i, i, p]
+        L.kda_compose_segments.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -297,6 +299,55 @@ def kda_output_gate_norm(o, z, eps=1e-6, y=None, stream=None):
     rows = o.numel() // D
     _check(lib().kda_output_gate_norm(_ptr(o), _ptr(z), _ptr(y), rows, D, float(eps), code, _stream(dev, stream)))
     return y
+
+
+def kda_chunk_fwd_split(q, k, v, a, beta, segments, initial_state=None, o=None, final_state=None, stream=None):
+    """kda_chunk_fwd with each sequence cut into `segments` pieces that run
+    side by side (the page's KCP decomposition on one device): two packed
+    runs give every segment's transition M (from S = I with v = 0) and
+    fragment E (from zero), kda_compose_segments the entering states, and a
+    third packed run the outputs and final states.  Three times the state
+    work, for `segments` times the parallelism: worth it when B * H leaves
+    most compute units idle.  Same arguments and results as kda_chunk_fwd
+    (up to rounding).  Buffers for the fragments come from torch; every step
+    of the arithmetic runs in the library's kernels."""
+    import torch
+
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    P = int(segments)
+    if P < 1:
+        raise ValueError("segments must be at least 1")
+    if P == 1 or T <= 16:
+        return kda_chunk_fwd(q, k, v, a, beta, initial_state=initial_state, o=o, final_state=final_state,
+                             stream=stream)
+    L = -(-T // P)
+    L = -(-L // 16) * 16  # segment length: whole chunks
+    P = -(-T // L)
+    starts = [j * L for j in range(P)]
+    cu = torch.tensor([b * T + s0 for b in range(B) for s0 in starts] + [B * T], dtype=torch.int32, device=dev)
+
+    def flat(x):
+        return x.reshape((B * T,) + tuple(x.shape[2:]))
+
+    qf, kf, vf, af, bf = flat(q), flat(k), flat(v), flat(a), flat(beta)
+    scratch = torch.empty_like(vf)
+    eye = torch.eye(Dk, dtype=torch.float32, device=dev).expand(B * P, H, Dk, Dk).contiguous()
+    _, M = kda_chunk_fwd_varlen(qf, kf, torch.zeros_like(vf), af, bf, cu, initial_state=eye, o=scratch, stream=stream)
+    _, E = kda_chunk_fwd_varlen(qf, kf, vf, af, bf, cu, o=scratch, stream=stream)
+    S_in = torch.empty_like(E)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (B, H, Dk, Dv), torch.float32, dev)
+    _check(lib().kda_compose_segments(_ptr(M), _ptr(E), _ptr(initial_state), _ptr(S_in), B, P, H, Dk, Dv,
+                                      _stream(dev, stream)))
+    _, S_all = kda_chunk_fwd_varlen(qf, kf, vf, af, bf, cu, initial_state=S_in, o=flat(o), stream=stream)
+    final_state.copy_(S_all.view(B, P, H, Dk, Dv)[:, P - 1])
+    return o, final_state
 
 
 def raw_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, stream=0):

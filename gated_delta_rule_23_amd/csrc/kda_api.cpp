@@ -215,6 +215,25 @@ kda_status kda_output_gate_norm(const void* o, const void* z, void* y, int64_t r
   return ok();
 }
 
+kda_status kda_compose_segments(const float* M, const float* E, const float* S0, float* S_in, int B, int P, int H,
+                                int Dk, int Dv, void* hip_stream) {
+  static const char* fn = "kda_compose_segments";
+  KDA_TRY(check_common(fn, B, H, Dk, Dv, KDA_F32));
+  if (P < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (P=%d)", fn, P);
+  if ((int64_t)B * H * P > kMaxUnits)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H*P exceeds the limit of %lld states", fn, (long long)kMaxUnits);
+  if ((int64_t)B * H == 0 || P == 0) return ok();
+  if (P > 1) {
+    KDA_TRY(check_ptr(fn, "M", M));
+    KDA_TRY(check_ptr(fn, "E", E));
+  }
+  if (S0) KDA_TRY(check_ptr(fn, "S0", S0));
+  KDA_TRY(check_ptr(fn, "S_in", S_in));
+  hipError_t e = kda::launch_compose(M, E, S0, S_in, B, P, H, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 const char* kda_status_string(kda_status status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";

@@ -37,6 +37,11 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
 hipError_t launch_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, float eps, bool bf16_io,
                                    hipStream_t stream);
 
+/* Entering states of P segments per (b, h) from their fragments (kda_compose.hip):
+ * M, E, S_in [B * P, H, 128, 128] (sequence b's segment j at b * P + j), S0 [B, H, 128, 128] or NULL. */
+hipError_t launch_compose(const float* M, const float* E, const float* S0, float* S_in, int B, int P, int H,
+                          hipStream_t stream);
+
 /* The bf16 I/O prefill (kda_prefill_bf16.hip); launch_chunk_fwd dispatches to it. */
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                  const float* initial_state, void* o, float* final_state, int B, int T, int H,

@@ -200,6 +200,25 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
 kda_status kda_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, int Dv, float eps,
                                 kda_dtype dtype, void* hip_stream);
 
+/*
+ * Entering states of P consecutive segments of each sequence, from their
+ * fragments: the page "Kimi K3：从三条信息流到完整系统", section "FlashKDA 与
+ * KCP", eq. (17).  A segment acts on its entering state as S -> M S + E
+ * (eq. (1) is affine in S): M is the segment's state run from S = I with
+ * v = 0, E its state run from zero, both from kda_chunk_fwd_varlen over the
+ * segments.  Then S_in[0] = S0 and S_in[j + 1] = M_j S_in[j] + E_j, in fp32.
+ * With S_in as the segments' initial states, kda_chunk_fwd_varlen gives the
+ * whole sequences' outputs and final states: the split of a long sequence
+ * over more compute units (gated_delta_rule_23_amd.kda_chunk_fwd_split).
+ *
+ *   M, E   [B * P, H, Dk, Dk] / [B * P, H, Dk, Dv] fp32 (read; segment j of
+ *          sequence b at b * P + j; the last segment's are not read)
+ *   S0     [B, H, Dk, Dv] fp32, or NULL for zeros (read)
+ *   S_in   [B * P, H, Dk, Dv] fp32 (written)
+ */
+kda_status kda_compose_segments(const float* M, const float* E, const float* S0, float* S_in, int B, int P, int H,
+                                int Dk, int Dv, void* hip_stream);
+
 /* Static text for a status code. */
 const char* kda_status_string(kda_status status);
 

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_chunk_fwd_states", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_decode_multi",
-              "kda_output_gate_norm", "kda_status_string", "kda_last_error", "kda_version"):
+              "kda_output_gate_norm", "kda_compose_segments", "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
 
@@ -124,6 +124,22 @@ def test_output_gate_norm_argument_checks(lib):
     assert call(eps=float("nan")) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call(dtype=5) == kda.KDA_ERR_INVALID_ARGUMENT
     assert kda.raw_output_gate_norm(None, None, None, 0, 128, 1e-6, 0) == kda.KDA_OK
+
+
+def test_compose_argument_checks(lib):
+    def call(**kw):
+        args = dict(M=P, E=P, S0=None, S_in=P, B=1, Pn=3, H=2, Dk=128, Dv=128)
+        args.update(kw)
+        return lib.kda_compose_segments(*args.values(), None)
+
+    lib.kda_compose_segments.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    for field in ("M", "E", "S_in"):
+        assert call(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT and field in kda.last_error()
+    assert call(S0=MIS) == kda.KDA_ERR_INVALID_ARGUMENT and "aligned" in kda.last_error()
+    assert call(Pn=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(Dk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert call(B=1 << 16, H=1 << 10, Pn=1 << 10) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(M=None, E=None, S_in=None, B=0) == kda.KDA_OK
 
 
 def multi(**kw):

@@ -483,6 +483,29 @@ def test_gate_variants_through_the_logits(kda, dtype, variant_name):
     assert max(errs) <= TOL[dtype]
 
 
+# --------------------------------------------------------------------------- sequence split
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("segments,with_s0", [(2, True), (4, False), (5, True)])
+def test_split_matches_oracle_and_plain(kda, dtype, segments, with_s0):
+    """Each sequence cut into segments (transition and fragment runs, the
+    composition kernel, the final run): outputs and final states against
+    the oracle and against kda_chunk_fwd."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=180 + segments, dtype=dtype, s0_scale=0.5 if with_s0 else None)
+    B, T, H = 2, 300, 3
+    print_case(f"case split {dtype} segments={segments} s0={with_s0} B={B} T={T} H={H}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, S = kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], x["beta"], segments, initial_state=x["s0"])
+    o1, S1 = run_prefill(kda, x, x["s0"])
+    o_ref, S_ref = oracle_block(w, nb=B, nt=T, nh=H)
+    e = [rel_l2(to_np(o), o_ref), rel_l2(to_np(S), S_ref), rel_l2(to_np(o), to_np(o1)), rel_l2(to_np(S), to_np(S1))]
+    print_case("  rel_l2 o/S vs oracle, vs kda_chunk_fwd: " + " ".join(f"{v:.2e}" for v in e))
+    assert max(e) <= TOL[dtype]
+
+
 # --------------------------------------------------------------------------- output gate and norm
 
 
