@@ -7,10 +7,11 @@
  * M_j is the segment's transition (its state run from S = I with v = 0) and
  * E_j its state run from zero; both come from the packed prefill.
  *
- * One 256-thread workgroup per (sequence b, head h), serial over the P
- * segments: the state in LDS (fp32, 64 KiB) and M_j staged transposed in LDS
- * (64 KiB); thread t computes row t / 2, columns 64 (t % 2) .. +63 of
- * M_j S + E_j in registers.  fp32 throughout.
+ * Each column of S evolves on its own (S -> M S + E acts on the rows), so a
+ * (sequence b, head h) takes kColGroups 256-thread workgroups of 16 columns
+ * each, serial over the P segments: its columns of S in LDS, M_j staged
+ * transposed in LDS (64 KiB, read by all of them); thread t computes row t / 2,
+ * columns 8 (t % 2) .. +7 of its group in registers.  fp32 throughout.
  */
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -19,39 +20,44 @@ namespace kda {
 namespace {
 
 constexpr int kComposeThreads = 256;
+constexpr int kColGroups = 8;
+constexpr int kGroupCols = kD / kColGroups;  // 16
 
 __global__ __launch_bounds__(kComposeThreads) void compose_kernel(const float* __restrict__ M,
                                                                   const float* __restrict__ E,
                                                                   const float* __restrict__ S0, float* __restrict__ S_in,
                                                                   int P, int H) {
-  __shared__ float s_state[kD][kD];  // S, row-major
-  __shared__ float s_mt[kD][kD];     // M_j transposed: s_mt[i][r] = M_j[r][i]
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
-  const int t = threadIdx.x, r = t >> 1, c0 = 64 * (t & 1);
-  auto state_at = [&](const float* base, int j) { return base + (((size_t)b * P + j) * H + h) * kD * kD; };
-  // S_in[0] = S0 (or zeros)
-  for (int e = t; e < kD * kD; e += kComposeThreads)
-    s_state[e / kD][e % kD] = S0 ? S0[((size_t)b * H + h) * kD * kD + e] : 0.0f;
+  __shared__ float s_state[kD][kGroupCols];  // this group's columns of S
+  __shared__ float s_mt[kD][kD];             // M_j transposed: s_mt[i][r] = M_j[r][i]
+  const int unit = blockIdx.x / kColGroups, g = blockIdx.x % kColGroups;
+  const int b = unit / H, h = unit % H;
+  const int t = threadIdx.x, r = t >> 1, cl = 8 * (t & 1), col = kGroupCols * g + cl;
+  auto at = [&](int j) { return (((size_t)b * P + j) * H + h) * kD * kD; };
+  for (int e = t; e < kD * kGroupCols; e += kComposeThreads) {
+    const int rr = e / kGroupCols, cc = e % kGroupCols;
+    s_state[rr][cc] = S0 ? S0[((size_t)b * H + h) * kD * kD + (size_t)rr * kD + kGroupCols * g + cc] : 0.0f;
+  }
   __syncthreads();
   for (int j = 0; j < P; ++j) {
-    float* out = S_in + (((size_t)b * P + j) * H + h) * kD * kD;
-    for (int e = t; e < kD * kD; e += kComposeThreads) out[e] = s_state[e / kD][e % kD];
+    float* out = S_in + at(j);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[(size_t)r * kD + col + c] = s_state[r][cl + c];
     if (j + 1 == P) break;
-    const float* Mj = state_at(M, j);
+    const float* Mj = M + at(j);
     for (int e = t; e < kD * kD; e += kComposeThreads) s_mt[e % kD][e / kD] = Mj[e];
     __syncthreads();
-    const float* Ej = state_at(E, j) + (size_t)r * kD + c0;
-    float acc[64];
+    const float* Ej = E + at(j) + (size_t)r * kD + col;
+    float acc[8];
 #pragma unroll
-    for (int c = 0; c < 64; ++c) acc[c] = Ej[c];
+    for (int c = 0; c < 8; ++c) acc[c] = Ej[c];
     for (int i = 0; i < kD; ++i) {
       const float m = s_mt[i][r];
 #pragma unroll
-      for (int c = 0; c < 64; ++c) acc[c] = fmaf(m, s_state[i][c0 + c], acc[c]);
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(m, s_state[i][cl + c], acc[c]);
     }
     __syncthreads();  // every thread has read S and M_j
 #pragma unroll
-    for (int c = 0; c < 64; ++c) s_state[r][c0 + c] = acc[c];
+    for (int c = 0; c < 8; ++c) s_state[r][cl + c] = acc[c];
     __syncthreads();
   }
 }
@@ -61,7 +67,8 @@ __global__ __launch_bounds__(kComposeThreads) void compose_kernel(const float* _
 hipError_t launch_compose(const float* M, const float* E, const float* S0, float* S_in, int B, int P, int H,
                           hipStream_t stream) {
   if (B == 0 || H == 0 || P == 0) return hipSuccess;
-  hipLaunchKernelGGL(compose_kernel, dim3((unsigned)(B * H)), dim3(kComposeThreads), 0, stream, M, E, S0, S_in, P, H);
+  hipLaunchKernelGGL(compose_kernel, dim3((unsigned)(B * H * kColGroups)), dim3(kComposeThreads), 0, stream, M, E, S0,
+                     S_in, P, H);
   return hipGetLastError();
 }
 
