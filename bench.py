@@ -191,6 +191,41 @@ def bench_gate_norm(w, reps=50):
     return dict(rows=rows, avg_ms=sum(ms) / len(ms), bytes=3 * rows * D * 2)
 
 
+def bench_split(cases=((8, 65536, 16), (32, 32768, 8)), reps=10):
+    """kda_chunk_fwd against kda_chunk_fwd_split on single sequences with
+    few heads (B = 1; H, T, segments per case), bf16, median launch times."""
+    import dataclasses
+
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+    from synth.workloads import WORKLOADS, device_inputs
+
+    out = []
+    for H, T, P in cases:
+        w = dataclasses.replace(WORKLOADS[1], B=1, H=H, T=T)
+        x = device_inputs(w)
+        o = torch.empty((1, T, H, D), dtype=torch.bfloat16, device="cuda")
+        S = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        times = {}
+        for name, segs in (("unsplit", 1), ("split", P)):
+            def one(segs=segs):
+                kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], x["beta"], segs, o=o, final_state=S,
+                                        stream=stream)
+
+            for _ in range(3):
+                one()
+            torch.cuda.synchronize()
+            ms = sorted(timed_launches(one, reps, stream))
+            times[name] = ms[len(ms) // 2]
+        out.append({"B": 1, "H": H, "T": T, "segments": P, "ms_unsplit": times["unsplit"], "ms_split": times["split"],
+                    "speedup": times["unsplit"] / times["split"]})
+        del x, o, S
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(reps=3):
     import torch
 
@@ -309,6 +344,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3],
                     help="prefill workload: 1 = B1 H96 T8192 (default), 2 = B4 H96 T32768 with S0, "
                          "3 = B1 H96 T1048576 mixed decay")
+    ap.add_argument("--split", action="store_true",
+                    help="also time kda_chunk_fwd_split against kda_chunk_fwd on single sequences with few heads")
     ap.add_argument("--decode-tokens", type=int, default=4,
                     help="tokens per kda_decode_multi call on the decode workload (1 skips that measurement)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -394,6 +431,8 @@ def main():
                         "frac": mf / FP32_VALU_PEAK, "algorithmic_flops_per_launch": mul["call_flops"]},
                 "kernel": "decode_multi_kernel",
             }
+    if args.split:
+        result["split"] = bench_split()
     if not args.no_cpu:
         threads = max(1, min(16, os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline(threads)
