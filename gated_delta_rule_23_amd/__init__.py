@@ -301,6 +301,9 @@ def kda_output_gate_norm(o, z, eps=1e-6, y=None, stream=None):
     return y
 
 
+_split_offsets = {}  # segment offsets of kda_chunk_fwd_split, per shape and device
+
+
 def kda_chunk_fwd_split(q, k, v, a, beta, segments, initial_state=None, o=None, final_state=None, stream=None):
     """kda_chunk_fwd with each sequence cut into `segments` pieces that run
     side by side (the page's KCP decomposition on one device): two packed
@@ -329,8 +332,12 @@ def kda_chunk_fwd_split(q, k, v, a, beta, segments, initial_state=None, o=None, 
     L = -(-T // P)
     L = -(-L // 16) * 16  # segment length: whole chunks
     P = -(-T // L)
-    starts = [j * L for j in range(P)]
-    cu = torch.tensor([b * T + s0 for b in range(B) for s0 in starts] + [B * T], dtype=torch.int32, device=dev)
+    key = (B, T, P, L, str(dev))
+    cu = _split_offsets.get(key)
+    if cu is None:  # made once per shape: a host-to-device copy would wait for the stream
+        starts = [j * L for j in range(P)]
+        cu = torch.tensor([b * T + s0 for b in range(B) for s0 in starts] + [B * T], dtype=torch.int32, device=dev)
+        _split_offsets[key] = cu
 
     def flat(x):
         return x.reshape((B * T,) + tuple(x.shape[2:]))
