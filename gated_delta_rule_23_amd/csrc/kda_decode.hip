@@ -363,6 +363,9 @@ hipError_t launch_decode_multi(const void* q, const void* k, const void* v, cons
                                float* state, void* o, const int* n_commit, int units, int H, int K, bool bf16_io,
                                hipStream_t stream) {
   if (units == 0 || K == 0) return hipSuccess;
+  // One token, every state committed: the [B, 1, H, .] rows are the single
+  // step's [B, H, .] rows, and its kernel streams the state faster.
+  if (K == 1 && !n_commit) return launch_decode(q, k, v, a, beta, state, o, units, bf16_io, stream);
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
