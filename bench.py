@@ -4,14 +4,19 @@ One step = one kda_chunk_fwd call over the prefill workload
 kda_prefill_bf16_b1_h96_t8192 (B=1, T=8192, H=96, d=128, bf16 q/k/v/a, fp32
 beta and state), inputs already resident in HBM.  Printed as one JSON line:
 value = tokens/s; `roofline` is the prefill kernel against HBM (its binding
-roof); `decode` adds kda_decode_step on the decode workload (256 sequences x
-96 heads, fp32 state updated in place, 64 steps with fresh inputs);
-`decode_multi` takes the same 64 tokens per state four at a time through
-kda_decode_multi (one state read and write per call); `cpu_baseline` is the
-fp64 oracle timed on a bounded sample on the host.
+roof), with `mfma` its algorithmic flops against the bf16 MFMA peak;
+`configs` times the other prefill workloads (the fp32 T=512 case, the
+4 x 32K batch with an initial state and, unless --no-long, the 1M-token
+sequence) with the same fields; `peaks` holds the HBM bandwidth and MFMA
+rates measured on the same box (a device copy and MFMA loops), and every
+fraction is also given against those; `decode` adds kda_decode_step on the
+decode workload (256 sequences x 96 heads, fp32 state updated in place, 64
+steps with fresh inputs); `decode_multi` takes the same 64 tokens per state
+four at a time through kda_decode_multi; `cpu_baseline` is the fp64 oracle
+timed on the host on the default workload, with stated samples of the others.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--decode-tokens K]
-                    [--workload 1|2|3]   (the other prefill workloads; 1 is the default line)
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-configs] [--no-long]
+                    [--decode-tokens K] [--workload 0|1|2|3]   (the prefill workload of the main line)
 """
 import argparse
 import hashlib
@@ -32,6 +37,7 @@ CHUNK = 16
 # channel) and beta (4 B), write o (2 B per channel); flops of the chunkwise
 # form at C = 16: 6 d^2 (the three state contractions) + 2 C (3 d + 2 d).
 BYTES_PER_TOKEN_HEAD_BF16 = 2 * (3 * D + D) + 4 + 2 * D   # 1284
+BYTES_PER_TOKEN_HEAD_F32 = 4 * (3 * D + D) + 4 + 4 * D    # 2564
 FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * CHUNK * (3 * D + 2 * D)  # 118784
 STATE_BYTES = D * D * 4
 # Decode, per (sequence, head) step: state read + written once, q/k/v/a in, o out.
@@ -41,6 +47,7 @@ DECODE_BYTES_PER_UNIT = 2 * STATE_BYTES + BYTES_PER_TOKEN_HEAD_BF16  # 132356
 # (a multiply and a multiply-add, 3 flops, per entry): 7 d^2 flops in all.
 DECODE_FLOPS_PER_UNIT = 7 * D * D  # 114688
 FP32_VALU_PEAK = 157.3e12  # MI355X fp32 vector, flop/s
+FP32_MFMA_PEAK = 157.3e12  # MI355X fp32 matrix, flop/s
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "chunk_fwd_bf16_kernel"  # the kernel the bf16 prefill workload runs
@@ -135,16 +142,21 @@ def timed_launches(fn, n, stream):
 
 
 def bench_prefill(steps, warmup, workload=1):
+    """kda_chunk_fwd over a whole prefill workload: warmup untimed launches,
+    then steps timed ones (HIP events around each on the launch stream)."""
     import torch
 
     import gated_delta_rule_23_amd as kda
     from synth.workloads import WORKLOADS, device_inputs
 
     w = WORKLOADS[workload]
+    t_gen = time.perf_counter()
     x = device_inputs(w)
-    o = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.empty((w.B, w.T, w.H, D), dtype=dt, device="cuda")
     S = torch.empty((w.B, w.H, D, D), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
     stream = torch.cuda.current_stream()
 
     def step():
@@ -158,13 +170,47 @@ def bench_prefill(steps, warmup, workload=1):
     per_launch = timed_launches(step, steps, stream)
     wall = time.perf_counter() - t0
     tokens = w.B * w.T
+    per_token_head = BYTES_PER_TOKEN_HEAD_BF16 if w.dtype == "bf16" else BYTES_PER_TOKEN_HEAD_F32
     # inputs and o per token-head, the final state written, and the initial state read when there is one
-    launch_bytes = (w.B * w.T * w.H * BYTES_PER_TOKEN_HEAD_BF16
+    launch_bytes = (w.B * w.T * w.H * per_token_head
                     + w.B * w.H * STATE_BYTES * (2 if x["s0"] is not None else 1))
     launch_flops = w.B * w.T * w.H * FLOPS_PER_TOKEN_HEAD
     avg_ms = sum(per_launch) / len(per_launch)
+    del x, o, S
+    torch.cuda.empty_cache()
     return dict(workload=w, tokens=tokens, wall=wall, per_launch_ms=per_launch, avg_ms=avg_ms,
-                launch_bytes=launch_bytes, launch_flops=launch_flops)
+                launch_bytes=launch_bytes, launch_flops=launch_flops, gen_s=t_gen)
+
+
+def prefill_fields(pre, peaks_measured):
+    """The roofline and MFMA fields of one prefill measurement."""
+    w = pre["workload"]
+    avg_s = pre["avg_ms"] / 1e3
+    achieved = pre["launch_bytes"] / avg_s
+    fl = pre["launch_flops"] / avg_s
+    mfma_peak = BF16_MFMA_PEAK if w.dtype == "bf16" else FP32_MFMA_PEAK
+    mfma_meas = (peaks_measured or {}).get("mfma_bf16_tflops" if w.dtype == "bf16" else "mfma_f32_tflops")
+    hbm_meas = (peaks_measured or {}).get("hbm_copy_gbs")
+    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK, "frac_of_measured_peak": achieved / 1e9 / hbm_meas if hbm_meas else None,
+            "kernel": PREFILL_KERNEL if w.dtype == "bf16" else "chunk_fwd_kernel", "launch_ms": pre["avg_ms"],
+            "algorithmic_bytes_per_launch": pre["launch_bytes"]}
+    mfma = {"algorithmic_flops_per_launch": pre["launch_flops"], "achieved_tflops": fl / 1e12,
+            "dtype": w.dtype, "peak_tflops": mfma_peak / 1e12, "frac": fl / mfma_peak,
+            "frac_of_measured_peak": fl / 1e12 / mfma_meas if mfma_meas else None}
+    return roof, mfma
+
+
+def measure_peaks():
+    """HBM copy and MFMA loop rates on this machine (peaks/)."""
+    import peaks
+
+    return {"hbm_copy_gbs": peaks.hbm_copy() / 1e9, "mfma_bf16_tflops": peaks.mfma(bf16=True) / 1e12,
+            "mfma_f32_tflops": peaks.mfma(bf16=False) / 1e12,
+            "spec": {"hbm_gbs": HBM_PEAK / 1e9, "mfma_bf16_tflops": BF16_MFMA_PEAK / 1e12,
+                     "mfma_f32_tflops": FP32_MFMA_PEAK / 1e12},
+            "how": "best of 5 launches of a 2 GiB device copy (16-byte non-temporal accesses; read + written "
+                   "bytes), and of loops of 8 independent 16x16x32 bf16 / 16x16x4 fp32 MFMAs on 4 waves per SIMD"}
 
 
 def bench_gate_norm(w, reps=50):
@@ -308,27 +354,105 @@ def bench_decode_multi(k_tokens, reps=3):
                 call_bytes=call_bytes, call_flops=call_flops, calls=len(calls), k=k_tokens, reps=reps)
 
 
-def cpu_baseline(threads):
-    """The oracle as it stands, on the prefill workload (all 96 heads, all
-    8192 tokens: about 30 core-seconds), on `threads` host threads.  Input
-    generation on the host is not timed."""
+def host_description():
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": cpu_model, "nproc": os.cpu_count(), "cpus_available": affinity, "rocm": rocm}
+
+
+def cpu_threads():
+    """The host threads the oracle uses: every CPU this process may run on,
+    at most 16 (the share of host CPUs a one-GPU machine grants a job)."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, avail))
+
+
+def _oracle_timed(w, threads, b0=0, nb=None, t0=0, nt=None, h0=0, nh=None):
+    """Regenerate a block of workload w on the host (not timed) and time the
+    oracle over it.  Returns (seconds, token-heads)."""
     import numpy as np
 
     import oracle
     import synth
-    from synth.workloads import WORKLOADS, host_inputs
+    from synth.workloads import host_inputs
 
-    w = WORKLOADS[1]
-    h = host_inputs(w, threads=threads)
+    h = host_inputs(w, b0=b0, nb=nb, t0=t0, nt=nt, h0=h0, nh=nh, threads=threads)
     args = (synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]), h["beta"].astype(np.float64))
     a = synth.to_f64(h["a"])
+    s0 = None if h["s0"] is None or t0 != 0 else h["s0"].astype(np.float64)
     del h
-    t0 = time.perf_counter()
-    oracle.forward(*args, a=a, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {w.name} workload ({w.B * w.T * w.H} token-heads) in {dt:.2f} s, "
-                      f"fp64, one thread per (batch, head) sequence"}
+    t = time.perf_counter()
+    oracle.forward(*args, a=a, s0=s0, threads=threads)
+    return time.perf_counter() - t, args[0].shape[0] * args[0].shape[1] * args[0].shape[2]
+
+
+def cpu_baseline(threads, others=True):
+    """The oracle as it stands, on the default prefill workload (all 96
+    heads, all 8192 tokens), and, with others, on stated samples of the
+    other workloads.  Input generation on the host is not timed."""
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS[1]
+    dt, th = _oracle_timed(w, threads)
+    out = {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole {w.name} workload ({th} token-heads) in {dt:.2f} s, "
+                     f"fp64, one thread per (batch, head) sequence", "host": host_description()}
+    if others:
+        per = {}
+        w0 = WORKLOADS[0]
+        dt0, th0 = _oracle_timed(w0, threads)
+        per[w0.name] = {"tokens_per_s": w0.B * w0.T / dt0, "s": dt0, "sample": f"whole ({th0} token-heads)"}
+        w2 = WORKLOADS[2]
+        dt2, th2 = _oracle_timed(w2, threads, h0=0, nh=8)
+        # tokens/s of the whole workload at the sample's rate: 8 of 96 heads were run
+        per[w2.name] = {"tokens_per_s": w2.B * w2.T * 8 / w2.H / dt2, "s": dt2,
+                        "sample": f"heads 0-7 of all 4 sequences, all 32768 tokens ({th2} token-heads); "
+                                  "tokens/s scaled to all 96 heads"}
+        w3 = WORKLOADS[3]
+        nt3 = 131072
+        dt3, th3 = _oracle_timed(w3, threads, nt=nt3, h0=0, nh=3)
+        per[w3.name] = {"tokens_per_s": nt3 * 3 / dt3 / w3.H, "s": dt3,
+                        "sample": f"heads 0-2, the first {nt3} tokens ({th3} token-heads); "
+                                  "tokens/s scaled to all 96 heads"}
+        w4 = WORKLOADS[4]
+        dt4, th4 = _oracle_timed(w4, threads, nb=64)
+        per[w4.name] = {"seq_steps_per_s": 64 * w4.H * w4.T / dt4 / w4.H, "s": dt4,
+                        "sample": f"64 of the 256 sequences, all 96 heads, all 64 steps ({th4} token-heads); "
+                                  "seq-steps/s counts (sequence, step) pairs over all heads"}
+        out["other_workloads"] = per
+    return out
+
+
+def log(msg):
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# The other prefill workloads timed beside the main line: (index, untimed warm-up, timed launches).
+OTHER_CONFIGS = ((2, 2, 10), (0, 3, 20), (3, 1, 3))
+
+
+def config_entry(pre, peaks_measured):
+    w = pre["workload"]
+    roof, mfma = prefill_fields(pre, peaks_measured)
+    return {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dtype": w.dtype, "initial_state": w.s0_scale is not None,
+            "tokens_per_s": pre["tokens"] / (pre["avg_ms"] / 1e3), "ms_per_launch": pre["avg_ms"],
+            "launches": len(pre["per_launch_ms"]), "roofline": roof, "mfma": mfma,
+            "input_generation_s": pre["gen_s"]}
 
 
 def main():
@@ -336,14 +460,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     # The prefill settles at its steady launch time after some 20 launches
     # (clock ramp): the default warm-up covers that, and the timed launches
-    # dominate the average a kernel trace of the same command reports.
+    # dominate the average a kernel trace of the same command reports.  The
+    # other workloads run first, so the main line's clock is warm whatever
+    # --warmup says.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3],
-                    help="prefill workload: 1 = B1 H96 T8192 (default), 2 = B4 H96 T32768 with S0, "
-                         "3 = B1 H96 T1048576 mixed decay")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other prefill workloads and the peaks")
+    ap.add_argument("--no-long", action="store_true", help="skip the 1M-token workload among the other workloads")
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3],
+                    help="prefill workload of the main line: 1 = B1 H96 T8192 (default), 0 = fp32 B1 H2 T512, "
+                         "2 = B4 H96 T32768 with S0, 3 = B1 H96 T1048576 mixed decay")
     ap.add_argument("--split", action="store_true",
                     help="also time kda_chunk_fwd_split against kda_chunk_fwd on single sequences with few heads")
     ap.add_argument("--decode-tokens", type=int, default=4,
@@ -367,12 +495,26 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
 
+    measured = None
+    others = []
+    if not args.no_configs:
+        measured = measure_peaks()
+        log(f"peaks: copy {measured['hbm_copy_gbs']:.0f} GB/s, bf16 MFMA {measured['mfma_bf16_tflops']:.0f} "
+            f"TFLOP/s, fp32 MFMA {measured['mfma_f32_tflops']:.1f} TFLOP/s")
+        for idx, warm, n in OTHER_CONFIGS:
+            if idx == args.workload or (idx == 3 and args.no_long):
+                continue
+            pre_i = bench_prefill(n, warm, idx)
+            others.append(config_entry(pre_i, measured))
+            log(f"workload {idx}: {pre_i['avg_ms']:.3f} ms per launch (inputs drawn in {pre_i['gen_s']:.1f} s)")
+
     pre = bench_prefill(args.steps, args.warmup, args.workload)
+    log(f"main line: {pre['avg_ms']:.4f} ms per launch")
     w = pre["workload"]
-    avg_s = pre["avg_ms"] / 1e3
     wall_per_step = pre["wall"] / args.steps
-    achieved = pre["launch_bytes"] / avg_s
-    traffic = measured_traffic(PREFILL_KERNEL) if args.workload == 1 else None  # counters taken on workload 1
+    roof, mfma = prefill_fields(pre, measured)
+    # counters were taken on the default workload
+    roof["traffic"] = measured_traffic(PREFILL_KERNEL) if args.workload == 1 else None
     result = {
         "metric": METRIC,
         "value": pre["tokens"] / wall_per_step,
@@ -384,18 +526,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": D, "d_v": D, "chunk": CHUNK,
-                   "io": "bf16 q/k/v/a/o, fp32 beta and state", "seed": w.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": traffic,
-                     "kernel": PREFILL_KERNEL, "launch_ms": pre["avg_ms"],
-                     "algorithmic_bytes_per_launch": pre["launch_bytes"]},
-        "mfma": {"algorithmic_flops_per_launch": pre["launch_flops"],
-                 "achieved_tflops": pre["launch_flops"] / avg_s / 1e12,
-                 "frac_of_bf16_peak": pre["launch_flops"] / avg_s / BF16_MFMA_PEAK},
+                   "io": f"{w.dtype} q/k/v/a/o, fp32 beta and state", "seed": w.seed},
+        "roofline": roof,
+        "mfma": mfma,
     }
+    if measured is not None:
+        result["peaks"] = measured
+        result["configs"] = others
     if args.workload == 1:
         # the eq. (6) epilogue over the prefill's output rows (o and the gate read, y written once)
         gn = bench_gate_norm(pre["workload"])
@@ -407,17 +547,21 @@ def main():
     if not args.no_decode:
         torch.cuda.empty_cache()
         dec = bench_decode()
+        log(f"decode: {dec['avg_step_ms']:.4f} ms per step")
         dach = dec["step_bytes"] / (dec["avg_step_ms"] / 1e3)
+        hbm_meas = measured["hbm_copy_gbs"] if measured else None
         result["decode"] = {
             "workload": dec["workload"].name, "value": dec["seq_steps_per_s"], "unit": "seq-steps/s",
             "steps": dec["steps"], "reps": dec["reps"], "ms_per_step": dec["avg_step_ms"],
             "roofline": {"bound": "hbm", "achieved": dach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK, "traffic": measured_traffic("decode_kernel"),
+                         "frac": dach / HBM_PEAK, "frac_of_measured_peak": dach / 1e9 / hbm_meas if hbm_meas else None,
+                         "traffic": measured_traffic("decode_kernel"),
                          "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec["step_bytes"]},
         }
         if args.decode_tokens > 1:
             torch.cuda.empty_cache()
             mul = bench_decode_multi(args.decode_tokens)
+            log(f"multi-token decode: {mul['avg_call_ms']:.4f} ms per call")
             mb = mul["call_bytes"] / (mul["avg_call_ms"] / 1e3)
             mf = mul["call_flops"] / (mul["avg_call_ms"] / 1e3)
             result["decode_multi"] = {
@@ -425,6 +569,7 @@ def main():
                 "unit": "seq-steps/s", "calls": mul["calls"], "reps": mul["reps"], "ms_per_call": mul["avg_call_ms"],
                 "vs_single_step": mul["seq_steps_per_s"] / dec["seq_steps_per_s"],
                 "hbm": {"achieved": mb / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": mb / HBM_PEAK,
+                        "frac_of_measured_peak": mb / 1e9 / hbm_meas if hbm_meas else None,
                         "algorithmic_bytes_per_launch": mul["call_bytes"]},
                 "traffic": measured_traffic("decode_multi_kernel"),
                 "alu": {"achieved": mf / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
@@ -434,8 +579,8 @@ def main():
     if args.split:
         result["split"] = bench_split()
     if not args.no_cpu:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        result["cpu_baseline"] = cpu_baseline(threads)
+        result["cpu_baseline"] = cpu_baseline(cpu_threads(), others=not args.no_configs)
+        log("oracle timed")
     print(json.dumps(result), flush=True)
 
 

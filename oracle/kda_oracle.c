@@ -6,18 +6,25 @@
  * may load it; the HIP library never links, includes or calls it, and it
  * shares no code with the HIP library.
  *
- * What it computes, per (batch, head) sequence, following the page
+ * What it computes, per (batch, head) sequence: eq. (1) of the page
  * "Kimi K3：从三条信息流到完整系统" (wineandchord.com), section
- * "KDA 是带逐通道遗忘的 delta rule", eq. (1) and its expanded form, and the
- * reference step printed there (decay first, then the delta correction, and
- * the output reads the state after the current token's write):
+ * "KDA 是带逐通道遗忘的 delta rule",
  *
- *   alpha_t = exp(g_t)                      (per key channel)
- *   S      <- Diag(alpha_t) S               (decay)
- *   e      =  v_t - S^T k_t                 (residual against the decayed prediction)
- *   S      <- S + beta_t k_t e^T            (delta write)
- *   o_t    =  S^T q_t                       (read after write)
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
  *
+ * evaluated token by token.  Multiplying out the product with
+ * X = Diag(alpha_t) S_{t-1} gives
+ *
+ *   S_t = X - beta_t k_t (k_t^T X) + beta_t k_t v_t^T = X + beta_t k_t (v_t - X^T k_t)^T,
+ *
+ * so each token costs O(d_k d_v) instead of forming the d_k x d_k matrix:
+ *
+ *   X     =  Diag(alpha_t) S_{t-1}         (the decay acts on the old state)
+ *   r     =  v_t - X^T k_t                 (r^T = v_t^T - k_t^T X)
+ *   S_t   =  X + beta_t k_t r^T
+ *   o_t   =  S_t^T q_t                     (the output reads the new state)
+ *
+ * with alpha_t = exp(g_t) per key channel.
  * The gate is eq. (5) of the section "下界 log-decay 是一个 kernel 设计":
  * g = g_min * sigmoid(x) with g_min = -5, where x already includes the
  * learned scale e^A (the caller passes x as the gate logit a).
@@ -47,7 +54,7 @@ void kda_oracle_gate(const double* a, double* g, int64_t n) {
 /* One sequence, T tokens, eq. (1) applied token by token. */
 static void kda_oracle_sequence(int T, int dk, int dv, const double* q, const double* k, const double* v,
                                 const double* gate, int gate_is_logit, const double* beta, const double* s0,
-                                double* o, double* S, double* alpha, double* e, double* states, int every) {
+                                double* o, double* S, double* alpha, double* r, double* states, int every) {
   if (s0) {
     memcpy(S, s0, sizeof(double) * (size_t)dk * dv);
   } else {
@@ -63,20 +70,20 @@ static void kda_oracle_sequence(int T, int dk, int dv, const double* q, const do
     /* alpha_t = exp(g_t), per key channel */
     for (int i = 0; i < dk; ++i) alpha[i] = exp(gate_is_logit ? kda_oracle_gate1(gt[i]) : gt[i]);
 
-    /* S <- Diag(alpha_t) S */
+    /* X = Diag(alpha_t) S_{t-1}, in place */
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha[i];
 
-    /* e = v_t - S^T k_t */
-    for (int j = 0; j < dv; ++j) e[j] = vt[j];
+    /* r = v_t - X^T k_t */
+    for (int j = 0; j < dv; ++j) r[j] = vt[j];
     for (int i = 0; i < dk; ++i)
-      for (int j = 0; j < dv; ++j) e[j] -= kt[i] * S[(size_t)i * dv + j];
+      for (int j = 0; j < dv; ++j) r[j] -= kt[i] * S[(size_t)i * dv + j];
 
-    /* S <- S + beta_t k_t e^T */
+    /* S_t = X + beta_t k_t r^T */
     for (int i = 0; i < dk; ++i)
-      for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bt * kt[i] * e[j];
+      for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bt * kt[i] * r[j];
 
-    /* o_t = S^T q_t */
+    /* o_t = S_t^T q_t */
     double* ot = o + (size_t)t * dv;
     for (int j = 0; j < dv; ++j) ot[j] = 0.0;
     for (int i = 0; i < dk; ++i)
@@ -98,11 +105,11 @@ typedef struct {
 static void* kda_oracle_worker(void* arg) {
   kda_oracle_job* j = (kda_oracle_job*)arg;
   double* alpha = (double*)malloc(sizeof(double) * (size_t)j->dk);
-  double* e = (double*)malloc(sizeof(double) * (size_t)j->dv);
-  if (!alpha || !e) {
+  double* r = (double*)malloc(sizeof(double) * (size_t)j->dv);
+  if (!alpha || !r) {
     j->failed = 1;
     free(alpha);
-    free(e);
+    free(r);
     return NULL;
   }
   size_t T = (size_t)j->T, dk = (size_t)j->dk, dv = (size_t)j->dv;
@@ -110,11 +117,11 @@ static void* kda_oracle_worker(void* arg) {
   for (int n = j->first; n < j->last; ++n) {
     kda_oracle_sequence(j->T, j->dk, j->dv, j->q + n * T * dk, j->k + n * T * dk, j->v + n * T * dv,
                         j->gate + n * T * dk, j->gate_is_logit, j->beta + n * T, j->s0 ? j->s0 + n * dk * dv : NULL,
-                        j->o + n * T * dv, j->s_final + n * dk * dv, alpha, e,
+                        j->o + n * T * dv, j->s_final + n * dk * dv, alpha, r,
                         j->states ? j->states + n * per_seq : NULL, j->every);
   }
   free(alpha);
-  free(e);
+  free(r);
   return NULL;
 }
 

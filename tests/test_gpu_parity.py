@@ -662,17 +662,25 @@ def test_decode_multi_against_oracle(kda, dtype, K):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_multi_one_token_is_a_decode_step(kda, dtype):
+    """K = 1: without commit counts the call is routed to the single-step
+    kernel (identical bits); with a commit count of 1 per row it runs the
+    multi-token kernel, whose layout must give the single step's result."""
     import torch
 
     w = variant(WORKLOADS[4], index=90, dtype=dtype)
     B, H = 4, 7
     x = device_inputs(w, B=B, T=1, H=H)
-    s1, s2 = x["s0"].clone(), x["s0"].clone()
+    s1, s2, s3 = x["s0"].clone(), x["s0"].clone(), x["s0"].clone()
     o1 = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], s1)
     o2 = kda.kda_decode_step(x["q"][:, 0].contiguous(), x["k"][:, 0].contiguous(), x["v"][:, 0].contiguous(),
                              x["a"][:, 0].contiguous(), x["beta"][:, 0].contiguous(), s2)
+    o3 = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], s3,
+                              n_commit=torch.full((B,), 1, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
-    assert rel_l2(to_np(o1[:, 0]), to_np(o2)) <= 1e-6 and rel_l2(to_np(s1), to_np(s2)) <= 1e-6
+    assert torch.equal(o1[:, 0], o2) and torch.equal(s1, s2)
+    e = [rel_l2(to_np(o3[:, 0]), to_np(o2)), rel_l2(to_np(s3), to_np(s2))]
+    print_case(f"  multi-token kernel at K = 1 vs the single step ({dtype}): rel_l2 o={e[0]:.2e} S={e[1]:.2e}")
+    assert max(e) <= 1e-6
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
