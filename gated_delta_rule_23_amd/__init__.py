@@ -14,6 +14,13 @@ is no fallback: if libkda.so is missing or was not built, every call raises.
     kda_output_gate_norm(o, z, eps=1e-6, y=None) -> y   (sigmoid(z) * RMSNorm(o), eq. (6) without W_o, W_g)
     kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None) -> o
         (K tokens per sequence; the state keeps the first n_commit[b] of them)
+    kda_chunk_fwd_gated / kda_decode_step_gated / kda_decode_multi_gated(..., gate=...)
+        (gate "channel" = KDA, "scalar" = one fp32 logit per token and head,
+        "none" = alpha = 1, the delta rule)
+    kda_chunk_fwd_norm(q, k, v, a, beta, z, eps=1e-6, ...) -> (y, final_state)
+        (the prefill with sigmoid(z) * RMSNorm(o) fused into its output store)
+    kda_chunk_fwd_split(q, k, v, a, beta, segments, ...) -> (o, final_state)
+        (each sequence cut into segments that run side by side)
 
 Layouts (contiguous CUDA tensors): q, k, v, a, o ``[B, T, H, 128]`` (prefill),
 ``[B, H, 128]`` (decode) or ``[B, K, H, 128]`` (several tokens) in bfloat16 or
@@ -28,6 +35,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_SCALAR, KDA_GATE_NONE = 0, 1, 2
+GATES = {"channel": KDA_GATE_CHANNEL, "scalar": KDA_GATE_SCALAR, "none": KDA_GATE_NONE}
 D = 128
 
 _lib = None
@@ -61,6 +70,18 @@ def lib():
         L.kda_output_gate_norm.restype = i
         L.kda_compose_segments.argtypes = [p, p, p, p, i, i, i, i, i, p]
         L.kda_compose_segments.restype = i
+        L.kda_chunk_fwd_gated.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd_gated.restype = i
+        L.kda_decode_step_gated.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, p]
+        L.kda_decode_step_gated.restype = i
+        L.kda_decode_multi_gated.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, p]
+        L.kda_decode_multi_gated.restype = i
+        L.kda_chunk_fwd_norm.argtypes = [p, p, p, p, p, p, p, ctypes.c_float, p, p, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd_norm.restype = i
+        L.kda_chunk_fwd_split_workspace.argtypes = [i, i, i, i]
+        L.kda_chunk_fwd_split_workspace.restype = ctypes.c_size_t
+        L.kda_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i, p, ctypes.c_size_t, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd_split.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -142,6 +163,91 @@ def kda_chunk_fwd(q, k, v, a, beta, initial_state=None, o=None, final_state=None
     _check(lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(initial_state), _ptr(o),
                                _ptr(final_state), B, T, H, Dk, Dv, code, _stream(dev, stream)))
     return o, final_state
+
+
+def _gate_code(gate):
+    if isinstance(gate, str):
+        if gate not in GATES:
+            raise ValueError(f"gate must be one of {sorted(GATES)}, got {gate!r}")
+        return GATES[gate]
+    if gate not in GATES.values():
+        raise ValueError(f"unknown gate {gate}")
+    return int(gate)
+
+
+def _require_gate(a, gate, rows_shape, dt, dev):
+    """a per key channel ([..., 128] in the I/O dtype), one fp32 logit per
+    token and head (rows_shape), or nothing."""
+    import torch
+
+    if gate == KDA_GATE_CHANNEL:
+        _require(a, "a", tuple(rows_shape) + (D,), dt, dev)
+    elif gate == KDA_GATE_SCALAR:
+        _require(a, "a", tuple(rows_shape), torch.float32, dev)
+    elif a is not None:
+        raise ValueError("gate 'none' reads no logits: pass a=None")
+
+
+def kda_chunk_fwd_gated(q, k, v, a, beta, gate="channel", initial_state=None, o=None, final_state=None, stream=None):
+    """kda_chunk_fwd with a choice of gate (kda_chunk_fwd_gated of
+    include/kda.h): "channel" (a [B, T, H, 128] like q), "scalar" (a
+    [B, T, H] float32, one logit per token and head) or "none" (a = None,
+    alpha = 1).  Returns (o, final_state)."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
+    B, T, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    g = _gate_code(gate)
+    _require(q, "q", (B, T, H, Dk), dt, dev)
+    _require(k, "k", (B, T, H, Dk), dt, dev)
+    _require(v, "v", (B, T, H, D), dt, dev)
+    _require_gate(a, g, (B, T, H), dt, dev)
+    _require(beta, "beta", (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (B, H, Dk, D), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, D), dtype=dt, device=dev)
+    _require(o, "o", (B, T, H, D), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, Dk, D), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", (B, H, Dk, D), torch.float32, dev)
+    _check(lib().kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                     _ptr(final_state), B, T, H, Dk, D, code, g, _stream(dev, stream)))
+    return o, final_state
+
+
+def kda_chunk_fwd_norm(q, k, v, a, beta, z, eps=1e-6, initial_state=None, y=None, final_state=None, stream=None):
+    """The prefill with the output gate and head-wise RMSNorm of eq. (6)
+    fused into its output (kda_chunk_fwd_norm of include/kda.h):
+    y = sigmoid(z) * o / sqrt(mean(o^2) + eps), z like o.  Returns
+    (y, final_state); o is never written."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
+    B, T, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, name in ((q, "q"), (k, "k"), (a, "a")):
+        _require(t, name, (B, T, H, Dk), dt, dev)
+    _require(v, "v", (B, T, H, D), dt, dev)
+    _require(z, "z", (B, T, H, D), dt, dev)
+    _require(beta, "beta", (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (B, H, Dk, D), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, D), dtype=dt, device=dev)
+    _require(y, "y", (B, T, H, D), dt, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, Dk, D), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", (B, H, Dk, D), torch.float32, dev)
+    _check(lib().kda_chunk_fwd_norm(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(initial_state), _ptr(z),
+                                    float(eps), _ptr(y), _ptr(final_state), B, T, H, Dk, D, code,
+                                    _stream(dev, stream)))
+    return y, final_state
 
 
 def kda_chunk_fwd_states(q, k, v, a, beta, state_every, initial_state=None, o=None, final_state=None, states=None,
@@ -250,6 +356,59 @@ def kda_decode_step(q, k, v, a, beta, state, o=None, stream=None):
     return o
 
 
+def kda_decode_step_gated(q, k, v, a, beta, state, gate="channel", o=None, stream=None):
+    """kda_decode_step with a choice of gate (kda_decode_step_gated of
+    include/kda.h): a [B, H, 128] like q ("channel"), [B, H] float32
+    ("scalar") or None ("none").  Returns o; state is updated in place."""
+    import torch
+
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, 128]")
+    B, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    g = _gate_code(gate)
+    _require(q, "q", (B, H, Dk), dt, dev)
+    _require(k, "k", (B, H, Dk), dt, dev)
+    _require(v, "v", (B, H, D), dt, dev)
+    _require_gate(a, g, (B, H), dt, dev)
+    _require(beta, "beta", (B, H), torch.float32, dev)
+    _require(state, "state", (B, H, Dk, D), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, D), dtype=dt, device=dev)
+    _require(o, "o", (B, H, D), dt, dev)
+    _check(lib().kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(state), _ptr(o), B, H,
+                                       Dk, D, code, g, _stream(dev, stream)))
+    return o
+
+
+def kda_decode_multi_gated(q, k, v, a, beta, state, gate="channel", n_commit=None, o=None, stream=None):
+    """kda_decode_multi with a choice of gate: a [B, K, H, 128] like q
+    ("channel"), [B, K, H] float32 ("scalar") or None ("none")."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, K, H, 128]")
+    B, K, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    g = _gate_code(gate)
+    _require(q, "q", (B, K, H, Dk), dt, dev)
+    _require(k, "k", (B, K, H, Dk), dt, dev)
+    _require(v, "v", (B, K, H, D), dt, dev)
+    _require_gate(a, g, (B, K, H), dt, dev)
+    _require(beta, "beta", (B, K, H), torch.float32, dev)
+    _require(state, "state", (B, H, Dk, D), torch.float32, dev)
+    if n_commit is not None:
+        _require(n_commit, "n_commit", (B,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((B, K, H, D), dtype=dt, device=dev)
+    _require(o, "o", (B, K, H, D), dt, dev)
+    _check(lib().kda_decode_multi_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(state), _ptr(o),
+                                        _ptr(n_commit), B, K, H, Dk, D, code, g, _stream(dev, stream)))
+    return o
+
+
 def kda_decode_multi(q, k, v, a, beta, state, n_commit=None, o=None, stream=None):
     """K tokens per sequence in one pass (kda_decode_multi of include/kda.h):
     q, k, v, a [B, K, H, 128]; beta [B, K, H]; n_commit None (all K) or an
@@ -301,59 +460,60 @@ def kda_output_gate_norm(o, z, eps=1e-6, y=None, stream=None):
     return y
 
 
-_split_offsets = {}  # segment offsets of kda_chunk_fwd_split, per shape and device
+def kda_chunk_fwd_split_workspace(B, T, H, segments):
+    """Bytes of workspace kda_chunk_fwd_split needs for this shape."""
+    return int(lib().kda_chunk_fwd_split_workspace(int(B), int(T), int(H), int(segments)))
 
 
-def kda_chunk_fwd_split(q, k, v, a, beta, segments, initial_state=None, o=None, final_state=None, stream=None):
+def kda_chunk_fwd_split(q, k, v, a, beta, segments, initial_state=None, o=None, final_state=None, workspace=None,
+                        stream=None):
     """kda_chunk_fwd with each sequence cut into `segments` pieces that run
-    side by side (the page's KCP decomposition on one device): two packed
-    runs give every segment's transition M (from S = I with v = 0) and
-    fragment E (from zero), kda_compose_segments the entering states, and a
-    third packed run the outputs and final states.  Three times the state
-    work, for `segments` times the parallelism: worth it when B * H leaves
-    most compute units idle.  Same arguments and results as kda_chunk_fwd
-    (up to rounding).  Buffers for the fragments come from torch; every step
-    of the arithmetic runs in the library's kernels."""
+    side by side (kda_chunk_fwd_split of include/kda.h: the page's KCP
+    decomposition on one device).  Same arguments and results as
+    kda_chunk_fwd (up to rounding).  workspace: a CUDA uint8 tensor of at
+    least kda_chunk_fwd_split_workspace(B, T, H, segments) bytes, or None
+    to take one from torch.  With a stream given, the workspace and the
+    outputs are allocated on that stream, so torch does not hand their
+    memory to other work before the stream is done with it."""
+    import contextlib
+
     import torch
 
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
     B, T, H, Dk = q.shape
-    Dv = v.shape[3]
-    dev = q.device
-    if o is None:
-        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
-    if final_state is None:
-        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
     P = int(segments)
     if P < 1:
         raise ValueError("segments must be at least 1")
-    if P == 1 or T <= 16:
-        return kda_chunk_fwd(q, k, v, a, beta, initial_state=initial_state, o=o, final_state=final_state,
-                             stream=stream)
-    L = -(-T // P)
-    L = -(-L // 16) * 16  # segment length: whole chunks
-    P = -(-T // L)
-    key = (B, T, P, L, str(dev))
-    cu = _split_offsets.get(key)
-    if cu is None:  # made once per shape: a host-to-device copy would wait for the stream
-        starts = [j * L for j in range(P)]
-        cu = torch.tensor([b * T + s0 for b in range(B) for s0 in starts] + [B * T], dtype=torch.int32, device=dev)
-        _split_offsets[key] = cu
-
-    def flat(x):
-        return x.reshape((B * T,) + tuple(x.shape[2:]))
-
-    qf, kf, vf, af, bf = flat(q), flat(k), flat(v), flat(a), flat(beta)
-    scratch = torch.empty_like(vf)
-    eye = torch.eye(Dk, dtype=torch.float32, device=dev).expand(B * P, H, Dk, Dk).contiguous()
-    _, M = kda_chunk_fwd_varlen(qf, kf, torch.zeros_like(vf), af, bf, cu, initial_state=eye, o=scratch, stream=stream)
-    _, E = kda_chunk_fwd_varlen(qf, kf, vf, af, bf, cu, o=scratch, stream=stream)
-    S_in = torch.empty_like(E)
+    for t, name in ((q, "q"), (k, "k"), (a, "a")):
+        _require(t, name, (B, T, H, Dk), dt, dev)
+    _require(v, "v", (B, T, H, D), dt, dev)
+    _require(beta, "beta", (B, T, H), torch.float32, dev)
     if initial_state is not None:
-        _require(initial_state, "initial_state", (B, H, Dk, Dv), torch.float32, dev)
-    _check(lib().kda_compose_segments(_ptr(M), _ptr(E), _ptr(initial_state), _ptr(S_in), B, P, H, Dk, Dv,
-                                      _stream(dev, stream)))
-    _, S_all = kda_chunk_fwd_varlen(qf, kf, vf, af, bf, cu, initial_state=S_in, o=flat(o), stream=stream)
-    final_state.copy_(S_all.view(B, P, H, Dk, Dv)[:, P - 1])
+        _require(initial_state, "initial_state", (B, H, Dk, D), torch.float32, dev)
+    if o is not None:
+        _require(o, "o", (B, T, H, D), dt, dev)
+    if final_state is not None:
+        _require(final_state, "final_state", (B, H, Dk, D), torch.float32, dev)
+    need = kda_chunk_fwd_split_workspace(B, T, H, P)
+    if workspace is not None:
+        _require(workspace, "workspace", tuple(workspace.shape), torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+    with ctx:
+        if o is None:
+            o = torch.empty((B, T, H, D), dtype=dt, device=dev)
+        if final_state is None:
+            final_state = torch.empty((B, H, Dk, D), dtype=torch.float32, device=dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check(lib().kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(initial_state),
+                                         _ptr(o), _ptr(final_state), P, _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(), B, T, H, Dk, D, code,
+                                         _stream(dev, stream)))
     return o, final_state
 
 
@@ -385,6 +545,30 @@ def raw_decode_multi(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtyp
 
 def raw_output_gate_norm(o, z, y, rows, Dv, eps, dtype, stream=0):
     return lib().kda_output_gate_norm(o, z, y, rows, Dv, eps, dtype, stream)
+
+
+def raw_chunk_fwd_gated(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, gate, stream=0):
+    return lib().kda_chunk_fwd_gated(q, k, v, a, beta, initial_state, o, final_state, B, T, H, Dk, Dv, dtype, gate,
+                                     stream)
+
+
+def raw_chunk_fwd_norm(q, k, v, a, beta, initial_state, z, eps, y, final_state, B, T, H, Dk, Dv, dtype, stream=0):
+    return lib().kda_chunk_fwd_norm(q, k, v, a, beta, initial_state, z, eps, y, final_state, B, T, H, Dk, Dv, dtype,
+                                    stream)
+
+
+def raw_chunk_fwd_split(q, k, v, a, beta, initial_state, o, final_state, segments, workspace, workspace_bytes, B, T,
+                        H, Dk, Dv, dtype, stream=0):
+    return lib().kda_chunk_fwd_split(q, k, v, a, beta, initial_state, o, final_state, segments, workspace,
+                                     workspace_bytes, B, T, H, Dk, Dv, dtype, stream)
+
+
+def raw_decode_step_gated(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, gate, stream=0):
+    return lib().kda_decode_step_gated(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, gate, stream)
+
+
+def raw_decode_multi_gated(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype, gate, stream=0):
+    return lib().kda_decode_multi_gated(q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype, gate, stream)
 
 
 def last_error():

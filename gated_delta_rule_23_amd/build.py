@@ -8,7 +8,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_prefill_bf16.hip", "kda_epilogue.hip",
-           "kda_compose.hip"]
+           "kda_compose.hip", "kda_split.hip"]
 
 # Packed fp32 VALU forms are kept out of the device code; the host pass does
 # not know the feature and says so, which is harmless.

@@ -84,12 +84,32 @@ hipError_t device_cu_count(hipStream_t stream, int* cus) {
 
 namespace {
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+/* The gate logits a: per key channel (16-byte aligned rows), one fp32 value
+ * per token and head (4-byte aligned), or not read. */
+kda_status check_gate(const char* fn, kda_gate gate, const void* a) {
+  switch (gate) {
+    case KDA_GATE_CHANNEL: return check_ptr(fn, "a", a);
+    case KDA_GATE_SCALAR:
+      if (!a) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: a is NULL", fn);
+      if (!aligned4(a)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: a is not 4-byte aligned", fn);
+      return KDA_OK;
+    case KDA_GATE_NONE: return KDA_OK;
+  }
+  return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate %d", fn, (int)gate);
+}
+
 kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* a,
-                          const float* beta, const float* initial_state, void* o, float* final_state, float* states,
-                          int state_every, const int* cu_seqlens, int B, int T, int H, int Dk, int Dv,
-                          kda_dtype dtype, void* hip_stream) {
+                          const float* beta, const float* initial_state, void* o, float* final_state,
+                          const kda::PrefillOptions& opt, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                          void* hip_stream) {
   KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
   if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
+  if (opt.gate != KDA_GATE_CHANNEL && opt.gate != KDA_GATE_SCALAR && opt.gate != KDA_GATE_NONE)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate %d", fn, opt.gate);
+  if (opt.z && !(opt.eps >= 0.0f && opt.eps <= 1.0e30f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
   const int64_t units = (int64_t)B * H;
   if (units == 0) return ok();
   // a chunk of one tensor (16 tokens x H x 128 elements) is addressed with 32-bit byte offsets
@@ -97,7 +117,7 @@ kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
     return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d exceeds the prefill limit of %d heads", fn, H, kMaxPrefillHeads);
   // every element index (b, t, h, channel) must fit in 63 bits: B*T*H*128 < 2^62
   // (packed sequences share the T rows: T*H*128)
-  if ((cu_seqlens ? 1.0 : (double)B) * (double)T * (double)H * 128.0 > 4.0e18)
+  if ((opt.cu_seqlens ? 1.0 : (double)B) * (double)T * (double)H * 128.0 > 4.0e18)
     return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*T*H*128 overflows the index range", fn);
   KDA_TRY(check_ptr(fn, "final_state", final_state));
   if (initial_state) KDA_TRY(check_ptr(fn, "initial_state", initial_state));
@@ -105,75 +125,50 @@ kda_status chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
     KDA_TRY(check_ptr(fn, "q", q));
     KDA_TRY(check_ptr(fn, "k", k));
     KDA_TRY(check_ptr(fn, "v", v));
-    KDA_TRY(check_ptr(fn, "a", a));
+    KDA_TRY(check_gate(fn, static_cast<kda_gate>(opt.gate), a));
     KDA_TRY(check_ptr(fn, "beta", beta));
     KDA_TRY(check_ptr(fn, "o", o));
+    if (opt.z) KDA_TRY(check_ptr(fn, "z", opt.z));
   }
-  if (states || state_every) {
-    if (state_every <= 0 || state_every % 16 != 0)
-      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_every=%d must be a positive multiple of 16", fn, state_every);
-    if (T / state_every > 0) KDA_TRY(check_ptr(fn, "states", states));
+  if (opt.states || opt.state_every) {
+    if (opt.state_every <= 0 || opt.state_every % 16 != 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_every=%d must be a positive multiple of 16", fn,
+                  opt.state_every);
+    if (T / opt.state_every > 0) KDA_TRY(check_ptr(fn, "states", opt.states));
   }
   hipError_t e = kda::launch_chunk_fwd(q, k, v, a, beta, initial_state, o, final_state, B, T, H, dtype == KDA_BF16,
-                                       static_cast<hipStream_t>(hip_stream), states, state_every, cu_seqlens);
+                                       static_cast<hipStream_t>(hip_stream), opt);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
-                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
-                         int Dv, kda_dtype dtype, void* hip_stream) {
-  return chunk_fwd_impl("kda_chunk_fwd", q, k, v, a, beta, initial_state, o, final_state, nullptr, 0, nullptr, B, T,
-                        H, Dk, Dv, dtype, hip_stream);
-}
-
-kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, const void* a, const float* beta,
-                                const float* initial_state, void* o, float* final_state, float* states,
-                                int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
-                                void* hip_stream) {
-  return chunk_fwd_impl("kda_chunk_fwd_states", q, k, v, a, beta, initial_state, o, final_state, states,
-                        state_every, nullptr, B, T, H, Dk, Dv, dtype, hip_stream);
-}
-
-kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* a, const float* beta,
-                                const int* cu_seqlens, const float* initial_state, void* o, float* final_state, int N,
-                                int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
-  static const char* fn = "kda_chunk_fwd_varlen";
-  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
-  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is not 4-byte aligned", fn);
-  return chunk_fwd_impl(fn, q, k, v, a, beta, initial_state, o, final_state, nullptr, 0, cu_seqlens, N, T, H, Dk, Dv,
-                        dtype, hip_stream);
-}
-
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,
-                           float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
-  static const char* fn = "kda_decode_step";
+kda_status decode_impl(const char* fn, const void* q, const void* k, const void* v, const void* a, const float* beta,
+                       float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, kda_gate gate,
+                       void* hip_stream) {
   KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate %d", fn, (int)gate);
   const int64_t units = (int64_t)B * H;
   if (units == 0) return ok();
   KDA_TRY(check_ptr(fn, "q", q));
   KDA_TRY(check_ptr(fn, "k", k));
   KDA_TRY(check_ptr(fn, "v", v));
-  KDA_TRY(check_ptr(fn, "a", a));
+  KDA_TRY(check_gate(fn, gate, a));
   KDA_TRY(check_ptr(fn, "beta", beta));
   KDA_TRY(check_ptr(fn, "state", state));
   KDA_TRY(check_ptr(fn, "o", o));
-  hipError_t e = kda::launch_decode(q, k, v, a, beta, state, o, (int)units, dtype == KDA_BF16,
+  hipError_t e = kda::launch_decode(q, k, v, a, beta, state, o, (int)units, dtype == KDA_BF16, (int)gate,
                                     static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 
-kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
-                            float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
-                            kda_dtype dtype, void* hip_stream) {
-  static const char* fn = "kda_decode_multi";
+kda_status decode_multi_impl(const char* fn, const void* q, const void* k, const void* v, const void* a,
+                             const float* beta, float* state, void* o, const int* n_commit, int B, int K, int H,
+                             int Dk, int Dv, kda_dtype dtype, kda_gate gate, void* hip_stream) {
   KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate %d", fn, (int)gate);
   if (K < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (K=%d)", fn, K);
   const int64_t units = (int64_t)B * H;
   if (units == 0 || K == 0) return ok();
@@ -185,16 +180,154 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v, const v
   KDA_TRY(check_ptr(fn, "q", q));
   KDA_TRY(check_ptr(fn, "k", k));
   KDA_TRY(check_ptr(fn, "v", v));
-  KDA_TRY(check_ptr(fn, "a", a));
+  KDA_TRY(check_gate(fn, gate, a));
   KDA_TRY(check_ptr(fn, "beta", beta));
   KDA_TRY(check_ptr(fn, "state", state));
   KDA_TRY(check_ptr(fn, "o", o));
-  if (n_commit && (reinterpret_cast<uintptr_t>(n_commit) & 3u) != 0)
+  if (n_commit && !aligned4(n_commit))
     return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_commit is not 4-byte aligned", fn);
   hipError_t e = kda::launch_decode_multi(q, k, v, a, beta, state, o, n_commit, (int)units, H, K, dtype == KDA_BF16,
-                                          static_cast<hipStream_t>(hip_stream));
+                                          (int)gate, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+/* Segments of the split: whole chunks of seg_len tokens, P of them covering T. */
+void split_shape(int T, int segments, int* P, int* seg_len) {
+  if (segments <= 1 || T <= 16) {
+    *P = 1;
+    *seg_len = T;
+    return;
+  }
+  int L = (T + segments - 1) / segments;
+  L = (L + 15) / 16 * 16;
+  *seg_len = L;
+  *P = (T + L - 1) / L;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                         int Dv, kda_dtype dtype, void* hip_stream) {
+  return chunk_fwd_impl("kda_chunk_fwd", q, k, v, a, beta, initial_state, o, final_state, kda::PrefillOptions(), B, T,
+                        H, Dk, Dv, dtype, hip_stream);
+}
+
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                               const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                               int Dv, kda_dtype dtype, kda_gate gate, void* hip_stream) {
+  kda::PrefillOptions opt;
+  opt.gate = (int)gate;
+  return chunk_fwd_impl("kda_chunk_fwd_gated", q, k, v, a, beta, initial_state, o, final_state, opt, B, T, H, Dk, Dv,
+                        dtype, hip_stream);
+}
+
+kda_status kda_chunk_fwd_norm(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                              const float* initial_state, const void* z, float eps, void* y, float* final_state, int B,
+                              int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_chunk_fwd_norm";
+  if (T > 0 && B > 0 && H > 0 && !z) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: z is NULL", fn);
+  kda::PrefillOptions opt;
+  opt.z = z;
+  opt.eps = eps;
+  return chunk_fwd_impl(fn, q, k, v, a, beta, initial_state, y, final_state, opt, B, T, H, Dk, Dv, dtype, hip_stream);
+}
+
+kda_status kda_chunk_fwd_states(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                const float* initial_state, void* o, float* final_state, float* states,
+                                int state_every, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                                void* hip_stream) {
+  kda::PrefillOptions opt;
+  opt.states = states;
+  opt.state_every = state_every;
+  return chunk_fwd_impl("kda_chunk_fwd_states", q, k, v, a, beta, initial_state, o, final_state, opt, B, T, H, Dk,
+                        Dv, dtype, hip_stream);
+}
+
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                const int* cu_seqlens, const float* initial_state, void* o, float* final_state, int N,
+                                int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_chunk_fwd_varlen";
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
+  if (!aligned4(cu_seqlens)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is not 4-byte aligned", fn);
+  kda::PrefillOptions opt;
+  opt.cu_seqlens = cu_seqlens;
+  return chunk_fwd_impl(fn, q, k, v, a, beta, initial_state, o, final_state, opt, N, T, H, Dk, Dv, dtype, hip_stream);
+}
+
+size_t kda_chunk_fwd_split_workspace(int B, int T, int H, int segments) {
+  if (B <= 0 || T <= 0 || H <= 0) return 0;
+  int P = 1, L = 0;
+  split_shape(T, segments, &P, &L);
+  return kda::split_workspace_bytes(B, P, H);
+}
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                               const float* initial_state, void* o, float* final_state, int segments,
+                               void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv,
+                               kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_chunk_fwd_split";
+  if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: segments=%d must be at least 1", fn, segments);
+  int P = 1, L = 0;
+  split_shape(T, segments, &P, &L);
+  // the same checks as the plain prefill, over B sequences of T tokens
+  KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
+  if ((int64_t)B * H * P > kMaxUnits)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H*segments exceeds the limit of %lld sequences", fn,
+                (long long)kMaxUnits);
+  if (P == 1 || (int64_t)B * H == 0)
+    return chunk_fwd_impl(fn, q, k, v, a, beta, initial_state, o, final_state, kda::PrefillOptions(), B, T, H, Dk, Dv,
+                          dtype, hip_stream);
+  const size_t need = kda::split_workspace_bytes(B, P, H);
+  if (!workspace) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (!aligned16(workspace)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace is not 16-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if (H > kMaxPrefillHeads)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d exceeds the prefill limit of %d heads", fn, H, kMaxPrefillHeads);
+  if ((double)B * (double)T * (double)H * 128.0 > 4.0e18)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*T*H*128 overflows the index range", fn);
+  KDA_TRY(check_ptr(fn, "final_state", final_state));
+  if (initial_state) KDA_TRY(check_ptr(fn, "initial_state", initial_state));
+  KDA_TRY(check_ptr(fn, "q", q));
+  KDA_TRY(check_ptr(fn, "k", k));
+  KDA_TRY(check_ptr(fn, "v", v));
+  KDA_TRY(check_ptr(fn, "a", a));
+  KDA_TRY(check_ptr(fn, "beta", beta));
+  KDA_TRY(check_ptr(fn, "o", o));
+  hipError_t e = kda::launch_split(q, k, v, a, beta, initial_state, o, final_state, B, T, H, P, L, dtype == KDA_BF16,
+                                   workspace, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                           float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+  return decode_impl("kda_decode_step", q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, KDA_GATE_CHANNEL, hip_stream);
+}
+
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                 float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, kda_gate gate,
+                                 void* hip_stream) {
+  return decode_impl("kda_decode_step_gated", q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, gate, hip_stream);
+}
+
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                            float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
+                            kda_dtype dtype, void* hip_stream) {
+  return decode_multi_impl("kda_decode_multi", q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype,
+                           KDA_GATE_CHANNEL, hip_stream);
+}
+
+kda_status kda_decode_multi_gated(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                  float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
+                                  kda_dtype dtype, kda_gate gate, void* hip_stream) {
+  return decode_multi_impl("kda_decode_multi_gated", q, k, v, a, beta, state, o, n_commit, B, K, H, Dk, Dv, dtype,
+                           gate, hip_stream);
 }
 
 kda_status kda_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, int Dv, float eps,
@@ -229,7 +362,7 @@ kda_status kda_compose_segments(const float* M, const float* E, const float* S0,
   }
   if (S0) KDA_TRY(check_ptr(fn, "S0", S0));
   KDA_TRY(check_ptr(fn, "S_in", S_in));
-  hipError_t e = kda::launch_compose(M, E, S0, S_in, B, P, H, static_cast<hipStream_t>(hip_stream));
+  hipError_t e = kda::launch_compose(M, E, S0, S_in, B, P, H, P, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }

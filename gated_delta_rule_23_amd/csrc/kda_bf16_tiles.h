@@ -46,6 +46,13 @@ __device__ __forceinline__ float quad_bcast(float x) {
   constexpr int ctrl = J | (J << 2) | (J << 4) | (J << 6);
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, true));  // folds into the user
 }
+/* The value of the lane N places further round this lane's 16-lane row
+ * (DPP row_ror:N, 1 <= N <= 15). */
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(N >= 1 && N <= 15, "row_ror takes 1 .. 15");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
 /* s_waitcnt vmcnt(0), the other counters untouched (gfx9 encoding). */
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8)); }
 /* Workgroup barrier (the same fences as __syncthreads).  Kernels whose waves

@@ -76,25 +76,49 @@ struct Smem {
   alignas(16) float prefix[kWaves][kChunk][4];  // per wave: [key channel][token group] partial sums of the gate
 };
 
+/* Run-time options of the general kernel (PrefillOptions of kda_internal.h,
+ * the checkpoint interval in chunks). */
+struct ChunkArgs {
+  float* states;
+  int state_every, n_states;
+  const int* cu_seqlens;
+  int seg_len, seg_count, last_only;
+  int mode, gate;
+};
+
 template <typename IO, typename OT>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                                                              const IO* __restrict__ v, const IO* __restrict__ a,
                                                              const float* __restrict__ beta,
                                                              const float* initial_state, IO* __restrict__ o,
-                                                             float* final_state, int T_all, int H,
-                                                             float* states, int state_every, int n_states,
-                                                             const int* cu_seqlens) {
+                                                             float* final_state, int T_all, int H, ChunkArgs args) {
   __shared__ Smem<OT> sm;
+  float* const states = args.states;
+  const int state_every = args.state_every, n_states = args.n_states;
+  const bool state_only = args.mode >= kModeFragment;      // no o
+  const bool transition = args.mode == kModeTransition;    // S0 = I, v = 0
+  const int gate_mode = args.gate;
   const int unit = blockIdx.x;  // b * H + h
   const int bb = unit / H, hh = unit % H;
-  // The sequence's first token and length: b T_all and T_all, or, for packed
+  // The sequence's first token and length: b T_all and T_all; for packed
   // sequences, cu_seqlens[b] .. cu_seqlens[b + 1] clamped to [0, T_all] (so
-  // any contents of cu_seqlens keep every access inside the tensors).
+  // any contents of cu_seqlens keep every access inside the tensors); for
+  // segments, segment j = b % seg_count of sequence b / seg_count.
   int64_t tok0 = (int64_t)bb * T_all;
   int T = T_all;
-  if (cu_seqlens) {
-    const int c0 = min(max(cu_seqlens[bb], 0), T_all);
-    const int c1 = min(max(cu_seqlens[bb + 1], c0), T_all);
+  int out_unit = unit;
+  bool write_final = true;
+  if (args.seg_len > 0) {
+    const int sb = bb / args.seg_count, j = bb % args.seg_count, s0 = j * args.seg_len;
+    tok0 = (int64_t)sb * T_all + s0;
+    T = max(0, min(args.seg_len, T_all - s0));
+    if (args.last_only) {
+      write_final = j == args.seg_count - 1;
+      out_unit = sb * H + hh;
+    }
+  } else if (args.cu_seqlens) {
+    const int c0 = min(max(args.cu_seqlens[bb], 0), T_all);
+    const int c1 = min(max(args.cu_seqlens[bb + 1], c0), T_all);
     tok0 = c0;
     T = c1 - c0;
   }
@@ -139,8 +163,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   // ---------------------------------------------------------------- state in
   f32x4 sacc[8];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt) sacc[rt] = f32x4{0, 0, 0, 0};
-  if (initial_state) {  // one test, so the loads issue back to back
+  for (int rt = 0; rt < 8; ++rt)  // zeros, or the identity for a transition run
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[rt][j] = transition && 16 * rt + 4 * h + j == col ? 1.0f : 0.0f;
+  if (initial_state && !transition) {  // one test, so the loads issue back to back
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -156,20 +182,26 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     float b[4];
   };
   // x: chunk index; rows_off / beta_off: x chunk strides in bytes
+  // (a scalar gate's fp32 logits are [.., H] like beta; with no gate a is not read)
+  const char* ga_seq = reinterpret_cast<const char*>(reinterpret_cast<const float*>(a) + tok0 * H + hh);
   auto load_gate_inputs = [&](int x, int64_t rows_off, int64_t beta_off, Regs& r) {
     const int nb = rows_bytes(x);
     const rsrc_t rq = make_rsrc(q_seq + rows_off, nb), rk = make_rsrc(k_seq + rows_off, nb),
-                 ra = make_rsrc(a_seq + rows_off, nb), rb = make_rsrc(b_seq + beta_off, beta_bytes(x));
+                 ra = make_rsrc(a_seq + rows_off, gate_mode == kGateChannel ? nb : 0),
+                 rg = make_rsrc(ga_seq + beta_off, gate_mode == kGateScalar ? beta_bytes(x) : 0),
+                 rb = make_rsrc(b_seq + beta_off, beta_bytes(x));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       r.q[j] = Raw<IO>::load(rq, off_row[j]);
       r.k[j] = Raw<IO>::load(rk, off_row[j]);
-      r.a[j] = Raw<IO>::load(ra, off_row[j]);
+      // the gate logit as fp32 bits (zero-sized resources return 0 without reading)
+      r.a[j] = gate_mode == kGateScalar ? __builtin_amdgcn_raw_buffer_load_b32(rg, off_beta[j], 0, 0)
+                                        : __float_as_uint(Raw<IO>::f32(Raw<IO>::load(ra, off_row[j])));
       r.b[j] = load_f32(rb, off_beta[j]);
     }
   };
   auto load_chain_inputs = [&](int x, int64_t rows_off, Regs& r) {
-    const rsrc_t rv = make_rsrc(v_seq + rows_off, rows_bytes(x));
+    const rsrc_t rv = make_rsrc(v_seq + rows_off, transition ? 0 : rows_bytes(x));  // v = 0 in a transition run
 #pragma unroll
     for (int j = 0; j < 4; ++j) r.v[j] = Raw<IO>::load(rv, off_row[j]);
   };
@@ -192,7 +224,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     float run = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float g2 = kGateLog2 * sigmoid_fast(Raw<IO>::f32(cur.a[j]));
+      // no gate: g = 0 (alpha = 1)
+      float g2 = gate_mode == kGateNone ? 0.0f : kGateLog2 * sigmoid_fast(__uint_as_float(cur.a[j]));
       if constexpr (decltype(ragged)::value) g2 = 4 * h + j < nvalid ? g2 : 0.0f;  // padded tokens: g = 0
       run += g2;
       b[j] = run;
@@ -285,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[rt], fkb[rt], fv);
       // O rows 4h .. 4h+3 of this column; stores past T are dropped
-      const rsrc_t ro = make_rsrc(o_seq + rows_next - 4 * rows_step, rows_bytes(x));
+      const rsrc_t ro = make_rsrc(o_seq + rows_next - 4 * rows_step, state_only ? 0 : rows_bytes(x));
 #pragma unroll
       for (int j = 0; j < 4; ++j) Raw<IO>::store(ro, off_row[j], pq[j] + da[j]);
       // checkpoint: the state after token 16 (x + 1), when that is a multiple of the interval
@@ -373,34 +406,44 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   }
 
   // ---------------------------------------------------------------- state out
+  if (write_final) {
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int row = 16 * rt + 4 * h + j;
-      final_state[((size_t)unit * kD + row) * kD + col] = sacc[rt][j];
-    }
+      for (int j = 0; j < 4; ++j) {
+        int row = 16 * rt + 4 * h + j;
+        final_state[((size_t)out_unit * kD + row) * kD + col] = sacc[rt][j];
+      }
+  }
 }
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                            bool bf16_io, hipStream_t stream, float* states, int state_every,
-                            const int* cu_seqlens) {
-  const int units = B * H;
+                            bool bf16_io, hipStream_t stream, const PrefillOptions& opt_in) {
+  PrefillOptions opt = opt_in;
+  const int seqs = opt.seg_len > 0 ? B * opt.seg_count : B;
+  const int units = seqs * H;
   if (units == 0) return hipSuccess;
   // the interval in chunks and the number of checkpoints (none: no checkpoint output)
-  const int every_chunks = states ? state_every / kChunk : 0;
-  const int n_states = states ? T / state_every : 0;
-  if (n_states == 0) states = nullptr;
+  const int every_tokens = opt.states ? opt.state_every : 0;
+  opt.n_states = opt.states ? T / every_tokens : 0;
+  opt.state_every = opt.states ? every_tokens / kChunk : 0;
+  if (opt.n_states == 0) opt.states = nullptr;
   if (bf16_io) {
-    return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream, states,
-                                 every_chunks, n_states, cu_seqlens);
-  } else {
-    hipLaunchKernelGGL((chunk_fwd_kernel<float, float>), dim3(units), dim3(kThreads), 0, stream, (const float*)q,
-                       (const float*)k, (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state,
-                       T, H, states, every_chunks, n_states, cu_seqlens);
+    if (opt.states) opt.mode = kModeEmit;
+    else if ((opt.cu_seqlens || opt.seg_len > 0) && opt.mode == kModePlain) opt.mode = kModePacked;
+    return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream, opt);
   }
-  return hipGetLastError();
+  const ChunkArgs args = {opt.states, opt.state_every, opt.n_states, opt.cu_seqlens, opt.seg_len, opt.seg_count,
+                          opt.last_only ? 1 : 0, opt.mode, opt.gate};
+  hipLaunchKernelGGL((chunk_fwd_kernel<float, float>), dim3(units), dim3(kThreads), 0, stream, (const float*)q,
+                     (const float*)k, (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state,
+                     T, H, args);
+  hipError_t e = hipGetLastError();
+  // fp32 I/O: the output gate and norm as a second pass over o
+  if (e == hipSuccess && opt.z != nullptr)
+    e = launch_output_gate_norm(o, opt.z, o, (int64_t)seqs * T * H, opt.eps, false, stream);
+  return e;
 }
 
 }  // namespace kda

@@ -40,7 +40,9 @@ constexpr int kRowGroups = kDecodeThreads / 32;  // thread t: rows t / 32 + kRow
 constexpr int kRowsPerThread = kD / kRowGroups;
 constexpr int kWorkgroupsPerCU = 4;
 
-template <typename IO>
+// kGate (GateMode): a per key channel, one fp32 logit per (b, h) (a read as
+// [units] fp32), or no gate (alpha = 1, a not read).
+template <typename IO, int kGate>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                                                      const IO* __restrict__ v, const IO* __restrict__ a,
                                                      const float* __restrict__ beta, float* __restrict__ state,
@@ -68,8 +70,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __rest
   for (int set = 0; unit < units; set ^= 1) {
     const size_t row = (size_t)unit * kD;
     if (t < kD) {
-      const float qi = to_f32(q[row + t]), ki = to_f32(k[row + t]), ai = to_f32(a[row + t]);
-      const float al = expf(kGateFloor / (1.0f + expf(-ai)));
+      const float qi = to_f32(q[row + t]), ki = to_f32(k[row + t]);
+      float al = 1.0f;
+      if constexpr (kGate == kGateChannel) al = expf(kGateFloor / (1.0f + expf(-to_f32(a[row + t]))));
+      if constexpr (kGate == kGateScalar)
+        al = expf(kGateFloor / (1.0f + expf(-reinterpret_cast<const float*>(a)[unit])));
       s_alpha[set][t] = al;
       s_ak[set][t] = al * ki;
       s_aq[set][t] = al * qi;
@@ -202,7 +207,7 @@ __device__ __forceinline__ void store4<bf16>(rsrc_t r, int off, f32x4 x) {
                                         off, 0, 0);
 }
 
-template <typename IO>
+template <typename IO, int kGate>
 __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v, const IO* __restrict__ a,
     const float* __restrict__ beta, float* __restrict__ state, IO* __restrict__ o, const int* __restrict__ n_commit,
@@ -241,14 +246,19 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
   };
   auto load_group = [&](int u, int g, Staged& in) {
     const rsrc_t rq = rows_rsrc(q, u), rk = rows_rsrc(k, u), ra = rows_rsrc(a, u), rv = rows_rsrc(v, u);
-    const rsrc_t rb = make_rsrc(beta + first_row(u), ((int64_t)(K - 1) * H + 1) * (int64_t)sizeof(float));
+    const int64_t scalar_bytes = ((int64_t)(K - 1) * H + 1) * (int64_t)sizeof(float);
+    const rsrc_t rb = make_rsrc(beta + first_row(u), scalar_bytes);
 #pragma unroll
     for (int i = 0; i < kStagePerThread; ++i) {
       const int j = kGroupTokens * g + kStagePerThread * sh + i;
       const int off = (j * tok_elems + sc) * (int)sizeof(IO);
       in.q[i] = Raw<IO>::load(rq, off);
       in.k[i] = Raw<IO>::load(rk, off);
-      in.a[i] = Raw<IO>::load(ra, off);
+      if constexpr (kGate == kGateChannel) in.a[i] = Raw<IO>::load(ra, off);
+      if constexpr (kGate == kGateScalar)  // [B, K, H] fp32, like beta
+        in.a[i] = __builtin_amdgcn_raw_buffer_load_b32(
+            make_rsrc(reinterpret_cast<const float*>(a) + first_row(u), scalar_bytes), j * H * (int)sizeof(float), 0, 0);
+      if constexpr (kGate == kGateNone) in.a[i] = 0;
       in.v[i] = Raw<IO>::load(rv, off);
       in.b[i] = load_f32(rb, j * H * (int)sizeof(float));
     }
@@ -280,8 +290,10 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
       float lg[kStagePerThread], run = 0.0f;
 #pragma unroll
       for (int i = 0; i < kStagePerThread; ++i) {
-        const float ai = Raw<IO>::f32(in.a[i]);
-        run += kGateFloor * kLog2e / (1.0f + expf(-ai));
+        if constexpr (kGate != kGateNone) {
+          const float ai = kGate == kGateChannel ? Raw<IO>::f32(in.a[i]) : __uint_as_float(in.a[i]);
+          run += kGateFloor * kLog2e / (1.0f + expf(-ai));
+        }
         lg[i] = run;
       }
       const float before = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(run), 0xB1, 0xf, 0xf, false));
@@ -359,13 +371,41 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
   }
 }
 
+namespace {
+
+template <int kGate>
+void launch_multi_gate(unsigned grid, hipStream_t stream, const void* q, const void* k, const void* v, const void* a,
+                       const float* beta, float* state, void* o, const int* n_commit, int units, int H, int K,
+                       bool bf16_io) {
+  if (bf16_io)
+    hipLaunchKernelGGL((decode_multi_kernel<bf16, kGate>), dim3(grid), dim3(kMultiThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o, n_commit, units, H, K);
+  else
+    hipLaunchKernelGGL((decode_multi_kernel<float, kGate>), dim3(grid), dim3(kMultiThreads), 0, stream,
+                       (const float*)q, (const float*)k, (const float*)v, (const float*)a, beta, state, (float*)o,
+                       n_commit, units, H, K);
+}
+
+template <int kGate>
+void launch_decode_gate(unsigned grid, hipStream_t stream, const void* q, const void* k, const void* v, const void* a,
+                        const float* beta, float* state, void* o, int units, bool bf16_io) {
+  if (bf16_io)
+    hipLaunchKernelGGL((decode_kernel<bf16, kGate>), dim3(grid), dim3(kDecodeThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o, units);
+  else
+    hipLaunchKernelGGL((decode_kernel<float, kGate>), dim3(grid), dim3(kDecodeThreads), 0, stream, (const float*)q,
+                       (const float*)k, (const float*)v, (const float*)a, beta, state, (float*)o, units);
+}
+
+}  // namespace
+
 hipError_t launch_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                float* state, void* o, const int* n_commit, int units, int H, int K, bool bf16_io,
-                               hipStream_t stream) {
+                               int gate, hipStream_t stream) {
   if (units == 0 || K == 0) return hipSuccess;
   // One token, every state committed: the [B, 1, H, .] rows are the single
   // step's [B, H, .] rows, and its kernel streams the state faster.
-  if (K == 1 && !n_commit) return launch_decode(q, k, v, a, beta, state, o, units, bf16_io, stream);
+  if (K == 1 && !n_commit) return launch_decode(q, k, v, a, beta, state, o, units, bf16_io, gate, stream);
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
@@ -373,32 +413,29 @@ hipError_t launch_decode_multi(const void* q, const void* k, const void* v, cons
   // and as many for the next state's)
   const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 1);
   const unsigned grid = (unsigned)(units < slots ? units : slots);
-  if (bf16_io) {
-    hipLaunchKernelGGL(decode_multi_kernel<bf16>, dim3(grid), dim3(kMultiThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o, n_commit, units, H, K);
-  } else {
-    hipLaunchKernelGGL(decode_multi_kernel<float>, dim3(grid), dim3(kMultiThreads), 0, stream, (const float*)q,
-                       (const float*)k, (const float*)v, (const float*)a, beta, state, (float*)o, n_commit, units,
-                       H, K);
-  }
+  if (gate == kGateScalar)
+    launch_multi_gate<kGateScalar>(grid, stream, q, k, v, a, beta, state, o, n_commit, units, H, K, bf16_io);
+  else if (gate == kGateNone)
+    launch_multi_gate<kGateNone>(grid, stream, q, k, v, a, beta, state, o, n_commit, units, H, K, bf16_io);
+  else
+    launch_multi_gate<kGateChannel>(grid, stream, q, k, v, a, beta, state, o, n_commit, units, H, K, bf16_io);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* a, const float* beta, float* state,
-                         void* o, int units, bool bf16_io, hipStream_t stream) {
+                         void* o, int units, bool bf16_io, int gate, hipStream_t stream) {
   if (units == 0) return hipSuccess;
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
   const int64_t slots = (int64_t)kWorkgroupsPerCU * (cus > 0 ? cus : 1);
   const unsigned grid = (unsigned)(units < slots ? units : slots);
-  if (bf16_io) {
-    hipLaunchKernelGGL(decode_kernel<bf16>, dim3(grid), dim3(kDecodeThreads), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)a, beta, state, (bf16*)o, units);
-  } else {
-    hipLaunchKernelGGL(decode_kernel<float>, dim3(grid), dim3(kDecodeThreads), 0, stream, (const float*)q,
-                       (const float*)k, (const float*)v, (const float*)a, beta, state, (float*)o, units);
-  }
+  if (gate == kGateScalar)
+    launch_decode_gate<kGateScalar>(grid, stream, q, k, v, a, beta, state, o, units, bf16_io);
+  else if (gate == kGateNone)
+    launch_decode_gate<kGateNone>(grid, stream, q, k, v, a, beta, state, o, units, bf16_io);
+  else
+    launch_decode_gate<kGateChannel>(grid, stream, q, k, v, a, beta, state, o, units, bf16_io);
   return hipGetLastError();
 }
 

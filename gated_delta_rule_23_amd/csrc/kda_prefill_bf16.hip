@@ -133,9 +133,17 @@ __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int
                : "memory", "m0");
 }
 
-// kEmit: also write the state checkpoints (every state_every chunks, n_states of them per sequence).
-// kVarlen: sequences packed along the token axis, delimited by cu_seqlens.
-template <int kCT, bool kEmit, bool kVarlen>
+// kMode (PrefillMode): kModeEmit also writes the state checkpoints (every
+// state_every chunks, n_states of them per sequence); from kModePacked on the
+// sequences are delimited by cu_seqlens or cut into segments of seg_len
+// tokens (seg_count per sequence); kModeFragment writes only the final
+// states; kModeTransition also starts every sequence from the identity and
+// reads no v (the segment's transition matrix).
+// kGate (kda_gate): the gate per key channel, one fp32 logit per token and
+// head, or none (alpha = 1).
+// kNorm (one workgroup per sequence only): y = sigmoid(z) * RMSNorm(O) is
+// stored in place of O (eq. (6) without its projections).
+template <int kCT, int kMode, int kGate, bool kNorm>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
                                                                   const bf16* __restrict__ v,
@@ -144,12 +152,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
                                                                   const float* initial_state, bf16* __restrict__ o,
                                                                   float* final_state, int T_all, int H, int unit0,
                                                                   int unit_end, float* states, int state_every,
-                                                                  int n_states, const int* cu_seqlens) {
+                                                                  int n_states, const int* cu_seqlens, int seg_len,
+                                                                  int seg_count, int last_only,
+                                                                  const bf16* __restrict__ z, float eps) {
   static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
+  static_assert(!kNorm || kCT == 2, "the fused norm needs every value channel of a row in one workgroup");
+  constexpr bool kEmit = kMode == kModeEmit;
+  constexpr bool kVarlen = kMode >= kModePacked;
+  constexpr bool kStateOnly = kMode >= kModeFragment;     // no O: neither Qh S nor A is formed
+  constexpr bool kTransition = kMode == kModeTransition;  // S0 = I, v = 0
   __shared__ Smem sm;
   __shared__ InQKA s_qka[3];
   __shared__ InV s_v[3];
   __shared__ InBeta s_beta[5];
+  __shared__ InBeta s_ga[kGate == kGateScalar ? 5 : 1];  // scalar gate logits of chunk x (slot x % 5)
   // This launch serves units (b * H + h) unit0 .. unit_end - 1.  kCT == 2:
   // workgroup i takes unit unit0 + i.  kCT == 1: workgroups come in groups of
   // 16, slots 0..7 taking column half 0 of units 8 grp .. 8 grp + 7 (from
@@ -165,11 +181,27 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   // any contents of cu_seqlens keep every access inside the tensors).
   int64_t tok0 = (int64_t)bb * T_all;
   int T = T_all;
+  // Where the final state goes: this unit's slot, or, for the last segment
+  // of a sequence cut into segments (last_only), the sequence's own slot.
+  int out_unit = unit;
+  bool write_final = true;
   if constexpr (kVarlen) {
-    const int c0 = min(max(cu_seqlens[bb], 0), T_all);
-    const int c1 = min(max(cu_seqlens[bb + 1], c0), T_all);
-    tok0 = c0;
-    T = c1 - c0;
+    if (seg_len > 0) {
+      // segment j of sequence sb: tokens j seg_len .. of the sequence's T_all
+      const int sb = bb / seg_count, j = bb % seg_count;
+      const int s0 = j * seg_len;
+      tok0 = (int64_t)sb * T_all + s0;
+      T = max(0, min(seg_len, T_all - s0));
+      if (last_only) {
+        write_final = j == seg_count - 1;
+        out_unit = sb * H + hh;
+      }
+    } else {
+      const int c0 = min(max(cu_seqlens[bb], 0), T_all);
+      const int c1 = min(max(cu_seqlens[bb + 1], c0), T_all);
+      tok0 = c0;
+      T = c1 - c0;
+    }
   }
   // The wave index is uniform; saying so keeps everything derived from it
   // (buffer resources, branch conditions) in scalar registers.
@@ -225,16 +257,24 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     }
   };
   // beta (loader 0, lanes 0..15: token l) and q, k or a (loaders 0..2) of chunk i+2
+  // (the scalar gate's fp32 logits, [.., H] like beta, come with beta from
+  // loader 0 and a's rows are not loaded; with no gate, neither)
+  const char* ga_seq = reinterpret_cast<const char*>(reinterpret_cast<const float*>(a) + tok0 * H + hh);
   auto load_qka = [&](int i, auto full) {
     constexpr bool kFull = decltype(full)::value;
-    if (ldw == 0 && lane < kChunk)
-      load_b32_to_lds(make_rsrc(beta_seq + (i + 2) * beta_step, kFull ? beta_full : beta_bytes(i + 2)),
+    if (ldw == 0 && lane < kChunk) {
+      const int nb = kFull ? beta_full : beta_bytes(i + 2);
+      load_b32_to_lds(make_rsrc(beta_seq + (i + 2) * beta_step, nb),
                       (uint32_t)(uintptr_t)(lds_void*)&s_beta[(i + 2) % 5].t[0], beta_off);
-    if (ldw < 3) dma_rows(i + 2, &s_qka[(i + 2) % 3].t[ldw][0][0], full);
+      if constexpr (kGate == kGateScalar)
+        load_b32_to_lds(make_rsrc(ga_seq + (i + 2) * beta_step, nb),
+                        (uint32_t)(uintptr_t)(lds_void*)&s_ga[(i + 2) % 5].t[0], beta_off);
+    }
+    if (ldw < (kGate == kGateChannel ? 3 : 2)) dma_rows(i + 2, &s_qka[(i + 2) % 3].t[ldw][0][0], full);
   };
   // v of chunk i-1 (loader 3), into the slot prep reads last at iteration i-1
   auto load_v = [&](int i, auto full) {
-    if (ldw == 3) dma_rows(i - 1, &s_v[(i + 2) % 3].t[0][0], full);
+    if (!kTransition && ldw == 3) dma_rows(i - 1, &s_v[(i + 2) % 3].t[0][0], full);
   };
   auto load_inputs = [&](int i, auto full) {
     load_qka(i, full);
@@ -305,13 +345,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     const int col0 = kCT == 2 ? 32 * c : 64 * half + 16 * c;
     const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
     f32x4 sacc[kCT][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][col0 + 16 ct + l%16]
-    const bool has_s0 = initial_state != nullptr;  // one test, so the loads below issue back to back
+    const bool has_s0 = !kTransition && initial_state != nullptr;  // one test, so the loads below issue back to back
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[ct][rt][j] = 0.0f;
+        for (int j = 0; j < 4; ++j)  // zeros, or the identity for a transition run
+          sacc[ct][rt][j] = kTransition && 16 * rt + 4 * h + j == col0 + 16 * ct + n ? 1.0f : 0.0f;
     if (has_s0) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct)
@@ -345,10 +386,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
-        const Frag4<bf16> fv =  // B layout of V, columns col0 + 16ct ..
-            f4(lds_tr(&s_v[x % 3].t[0][0] + in_off(4 * h + (n >> 2), col0 + 16 * ct + 4 * (n & 3))));
-        f32x4 uc = {0, 0, 0, 0};
-        mfma_k16(uc, fm, fv);
+        f32x4 uc = {0, 0, 0, 0};  // v = 0 in a transition run: U = 0
+        if constexpr (!kTransition) {
+          const Frag4<bf16> fv =  // B layout of V, columns col0 + 16ct ..
+              f4(lds_tr(&s_v[x % 3].t[0][0] + in_off(4 * h + (n >> 2), col0 + 16 * ct + 4 * (n & 3))));
+          mfma_k16(uc, fm, fv);
+        }
         u_out[ct] = uc;
       }
     };
@@ -363,9 +406,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       for (int kb = 0; kb < 4; ++kb) {
         const int lo = 32 * kb * kChunk + tr_sw, hi = lo + 16 * kChunk;
         fw[kb] = cat8(lds_tr(tw + lo), lds_tr(tw + hi));
-        fq[kb] = cat8(lds_tr(tq + lo), lds_tr(tq + hi));
+        if constexpr (!kStateOnly) fq[kb] = cat8(lds_tr(tq + lo), lds_tr(tq + hi));
       }
-      const Frag4<bf16> fa = f4(lds_b64(&sm.r5[x % 5].am[0][0] + pl_sw));  // A layout of A
+      Frag4<bf16> fa;
+      if constexpr (!kStateOnly) fa = f4(lds_b64(&sm.r5[x % 5].am[0][0] + pl_sw));  // A layout of A
       Frag4<bf16> fkb[8];
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) fkb[rt] = f4(lds_b64(tb + 16 * rt * kChunk + pl_sw));  // A layout of Kb^T
@@ -382,32 +426,38 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         pq[ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mfma_k32(pw[ct], fw[kb], sf[kb]);
+        if constexpr (!kStateOnly) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mfma_k32(pq[ct], fq[kb], sf[kb]);
+          for (int kb = 0; kb < 4; ++kb) mfma_k32(pq[ct], fq[kb], sf[kb]);
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
-        // Diag(Gamma_C) S, under the MFMAs above
+        // Diag(Gamma_C) S, under the MFMAs above (alpha = 1 without a gate)
+        if constexpr (kGate != kGateNone) {
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-          float g = rt < 4 ? g_lo[rt] : g_hi[rt - 4];
-          if (ct == 1) asm volatile("" : "+v"(g));  // a separate copy, so each broadcast folds into its multiply
-          sacc[ct][rt][0] *= quad_bcast<0>(g);
-          sacc[ct][rt][1] *= quad_bcast<1>(g);
-          sacc[ct][rt][2] *= quad_bcast<2>(g);
-          sacc[ct][rt][3] *= quad_bcast<3>(g);
+          for (int rt = 0; rt < 8; ++rt) {
+            float g = rt < 4 ? g_lo[rt] : g_hi[rt - 4];
+            if (ct == 1) asm volatile("" : "+v"(g));  // a separate copy, so each broadcast folds into its multiply
+            sacc[ct][rt][0] *= quad_bcast<0>(g);
+            sacc[ct][rt][1] *= quad_bcast<1>(g);
+            sacc[ct][rt][2] *= quad_bcast<2>(g);
+            sacc[ct][rt][3] *= quad_bcast<3>(g);
+          }
         }
         // Vt = U - W S (zero for padded tokens: U and W have zero rows there)
         const Frag4<bf16> fv = frag4<bf16>(u[ct] - pw[ct]);
         f32x4 da = {0, 0, 0, 0};
-        mfma_k16(da, fa, fv);
+        if constexpr (!kStateOnly) mfma_k16(da, fa, fv);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) mfma_k16(sacc[ct][rt], fkb[rt], fv);
-        // O = Qh S + A Vt into the token-major tile; stored from there next iteration
-        const bf16x4 ob = pack_bf16x4(pq[ct] + da);
-        bf16* ot = &sm.r2[x & 1].ost[4 * h][col0 + 16 * ct + n];
+        if constexpr (!kStateOnly) {
+          // O = Qh S + A Vt into the token-major tile; stored from there next iteration
+          const bf16x4 ob = pack_bf16x4(pq[ct] + da);
+          bf16* ot = &sm.r2[x & 1].ost[4 * h][col0 + 16 * ct + n];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
+          for (int j = 0; j < 4; ++j) ot[j * kORow] = ob[j];
+        }
       }
     };
     // The state after chunk x (token 16 (x + 1)) into checkpoint (x + 1) / state_every - 1.  The
@@ -428,6 +478,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     // wave 0 (no Gram or solve) stores this workgroup's 128-byte half of all 16
     // rows, lane (n, h) rows 2h + n/8 and 8 + 2h + n/8.  Two tiles: chain wave
     // c stores rows 4c .. 4c+3.
+    u32x4 zbuf = {0, 0, 0, 0};  // z rows of the O tile stored next (kNorm)
     auto store_o = [&](int x, auto all) {
       const rsrc_t ro = make_rsrc(o_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
       auto store_row = [&](int tok, int cb) {
@@ -439,9 +490,43 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           store_row(2 * h + (n >> 3), 128 * half + 16 * (n & 7));
           store_row(8 + 2 * h + (n >> 3), 128 * half + 16 * (n & 7));
         }
+      } else if constexpr (kNorm) {
+        // y = sigmoid(z) o / sqrt(mean(o^2) + eps) over the row's 128 value
+        // channels: lane (n, h) holds channels 8n .. 8n+7 of token 4c + h,
+        // and the 16 lanes of a DPP row hold the whole row.
+        const int tok = 4 * c + h;
+        const u32x4 ov = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + 16 * n);
+        float f[8], ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = __uint_as_float(ov[e] << 16);
+          f[2 * e + 1] = __uint_as_float(ov[e] & 0xffff0000u);
+          ss = fmaf(f[2 * e], f[2 * e], ss);
+          ss = fmaf(f[2 * e + 1], f[2 * e + 1], ss);
+        }
+        ss += row_ror<8>(ss);
+        ss += row_ror<4>(ss);
+        ss += row_ror<2>(ss);
+        ss += row_ror<1>(ss);
+        const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / kD, eps));
+        u32x4 yv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y0 = f[2 * e] * r * sigmoid_fast(__uint_as_float(zbuf[e] << 16));
+          const float y1 = f[2 * e + 1] * r * sigmoid_fast(__uint_as_float(zbuf[e] & 0xffff0000u));
+          const bf16x2 yb = __builtin_convertvector(f32x2{y0, y1}, bf16x2);  // round to nearest even
+          yv[e] = __builtin_bit_cast(uint32_t, yb);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(yv, ro, tok * tok_bytes + 16 * n, 0, 0);
       } else {
         store_row(4 * c + h, 16 * n);
       }
+    };
+    // z of chunk x for the fused norm, one iteration before its rows are stored
+    const char* z_seq = reinterpret_cast<const char*>(z + seq_off);
+    auto load_z = [&](int x, auto all) {
+      const rsrc_t rz = make_rsrc(z_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
+      zbuf = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (4 * c + h) * tok_bytes + 16 * n, 0, 0));
     };
 
     // With the loads here, beta, q, k and a of chunk x land during
@@ -463,7 +548,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       constexpr int kRoleOf[kChainWaves] = {3, 0, 1, 2};
       const int r = kRole >= 0 ? kRole : kRoleOf[c];
       // the stores go out before the input loads, which wait_inputs then leaves in flight
-      if (kAll || (i >= 5 && i - 5 < nchunks)) store_o(i - 5, all);
+      if (!kStateOnly && (kAll || (i >= 5 && i - 5 < nchunks))) store_o(i - 5, all);
+      if (kNorm && (kAll || (i >= 4 && i - 4 < nchunks))) load_z(i - 4, all);
       if constexpr (kLoadsOnChain) load_qka(i, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
       if constexpr (kLoadsOnChain) load_v(i, all);
@@ -474,7 +560,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           next_emit += state_every;
         }
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 0) gram(i - 1, std::true_type(), std::false_type());
-      if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1) gram(i - 1, std::false_type(), std::true_type());
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1 && !kStateOnly)
+        gram(i - 1, std::false_type(), std::true_type());
       if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 2) solve(i - 2);
       if constexpr (kLoadsOnChain) {
         wait_inputs();
@@ -508,17 +595,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     else
       steady(std::integral_constant<int, 3>());
     for (; i < nsteps; i += 2) step2(i, std::false_type(), RunTimeRole());
-    if (nchunks > 0 && nsteps < nchunks + 5) store_o(nchunks - 1, std::false_type());  // not reached inside the loop
+    if (!kStateOnly && nchunks > 0 && nsteps < nchunks + 5)
+      store_o(nchunks - 1, std::false_type());  // not reached inside the loop
 
+    if (write_final) {
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct)
+      for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+        for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const size_t idx = ((size_t)unit * kD + 16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n;
-          final_state[idx] = sacc[ct][rt][j];
-        }
+          for (int j = 0; j < 4; ++j) {
+            const size_t idx = ((size_t)out_unit * kD + 16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n;
+            final_state[idx] = sacc[ct][rt][j];
+          }
+    }
   } else {
     // ================================================================ gate wave g: key channels 32g .. 32g+31
     const int g = wave - kChainWaves;
@@ -537,12 +627,63 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         const int off = in_off(4 * h + (n >> 2), 32 * g + 16 * cs + 4 * (n & 3));
         in.q[cs] = lds_tr(tile + off);
         in.k[cs] = lds_tr(tile + kChunk * kD + off);
-        in.a[cs] = lds_tr(tile + 2 * kChunk * kD + off);
+        if constexpr (kGate == kGateChannel) in.a[cs] = lds_tr(tile + 2 * kChunk * kD + off);
       }
     };
     // 0/1 weights of the two exchanged partial sums in this lane's exclusive prefix
     const float w_odd = (h & 1) ? 1.0f : 0.0f, w_hi = h >= 2 ? 1.0f : 0.0f;
     auto gate = [&](int x, const GateIn& in, auto ragged) {
+      if constexpr (kGate == kGateNone) {
+        // alpha = 1: Gamma = Gamma_C = 1, so Kh = Kt = Kb = K and Qh = Q (the
+        // chain skips the decay multiply); the bf16 inputs go out unchanged.
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+          const int cm = (32 * g + 16 * cs) * kChunk + pl_sw;
+          *reinterpret_cast<bf16x4*>(&sm.r4[x & 3].kh[0][0] + cm) = in.k[cs];
+          if constexpr (!kStateOnly) *reinterpret_cast<bf16x4*>(&sm.r5[x % 5].qh[0][0] + cm) = in.q[cs];
+          *reinterpret_cast<bf16x4*>(&sm.r2[x & 1].kt[0][0] + cm) = in.k[cs];
+          *reinterpret_cast<bf16x4*>(&sm.r5[x % 5].kb[0][0] + cm) = in.k[cs];
+        }
+        return;
+      }
+      if constexpr (kGate == kGateScalar) {
+        // One logit per token: sigmoid, the cumulative sums and the four
+        // decay factors are per token, shared by both channel tiles.
+        const f32x4 la = *reinterpret_cast<const f32x4*>(&s_ga[x % 5].t[4 * h]);
+        float b[4], run = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float sg = sigmoid_fast(la[j]);
+          if constexpr (decltype(ragged)::value) sg = x * kChunk + 4 * h + j < T ? sg : 0.0f;  // padded tokens: g = 0
+          run += sg;
+          b[j] = run;
+        }
+        const auto eo = __builtin_amdgcn_permlane16_swap(__float_as_uint(run), __float_as_uint(run), false, false);
+        const float e = __uint_as_float(eo[0]), pair = e + __uint_as_float(eo[1]);
+        const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+        const float z_lo = __uint_as_float(zz[0]);
+        const float prefix = kGateLog2 * fmaf(w_hi, z_lo, w_odd * e);
+        const float gam_c = __builtin_amdgcn_exp2f(kGateLog2 * (z_lo + __uint_as_float(zz[1])));
+        f32x4 gam, inv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float b2 = fmaf(kGateLog2, b[j], prefix);
+          gam[j] = __builtin_amdgcn_exp2f(b2);
+          inv[j] = __builtin_amdgcn_exp2f(-b2);
+        }
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+          const f32x4 kk = bf16x4_to_f32(in.k[cs]), qq = bf16x4_to_f32(in.q[cs]);
+          const f32x4 kt = kk * inv;
+          const int cm = (32 * g + 16 * cs) * kChunk + pl_sw;
+          lds_put(&sm.r4[x & 3].kh[0][0] + cm, kk * gam);
+          if constexpr (!kStateOnly) lds_put(&sm.r5[x % 5].qh[0][0] + cm, qq * gam);
+          lds_put(&sm.r2[x & 1].kt[0][0] + cm, kt);
+          lds_put(&sm.r5[x % 5].kb[0][0] + cm, kt * gam_c);
+          if (h == 0) sm.r5[x % 5].gamma_c[n >> 2][n & 3][2 * g + cs] = gam_c;
+        }
+        return;
+      }
       // Sums are kept in units of sigmoid(a); g log2(e) = kGateLog2 sigmoid(a).
       float b[2][4], run[2];
 #pragma unroll
@@ -583,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         }
         const int cm = (32 * g + 16 * cs) * kChunk + pl_sw;  // channel ch, tokens 4h ..
         lds_put(&sm.r4[x & 3].kh[0][0] + cm, kh);
-        lds_put(&sm.r5[x % 5].qh[0][0] + cm, qh);
+        if constexpr (!kStateOnly) lds_put(&sm.r5[x % 5].qh[0][0] + cm, qh);
         lds_put(&sm.r2[x & 1].kt[0][0] + cm, kt);
         lds_put(&sm.r5[x % 5].kb[0][0] + cm, kb);
         if (h == 0) sm.r5[x % 5].gamma_c[n >> 2][n & 3][2 * g + cs] = gam_c;
@@ -620,29 +761,63 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 
 }  // namespace
 
+namespace {
+
+typedef void (*PrefillKernel)(const bf16*, const bf16*, const bf16*, const bf16*, const float*, const float*, bf16*,
+                              float*, int, int, int, int, float*, int, int, const int*, int, int, int, const bf16*,
+                              float);
+
+/* The kernel for a layout, mode, gate and norm; the gate variants and the
+ * fused norm exist for the plain mode only (the norm with one workgroup per
+ * sequence), others return NULL. */
+template <int kCT>
+PrefillKernel pick_kernel(int mode, int gate, bool norm) {
+  if (norm) {
+    if constexpr (kCT == 2) {
+      if (mode == kModePlain && gate == kGateChannel) return chunk_fwd_bf16_kernel<2, kModePlain, kGateChannel, true>;
+    }
+    return nullptr;
+  }
+  if (gate == kGateScalar) return mode == kModePlain ? chunk_fwd_bf16_kernel<kCT, kModePlain, kGateScalar, false> : nullptr;
+  if (gate == kGateNone) return mode == kModePlain ? chunk_fwd_bf16_kernel<kCT, kModePlain, kGateNone, false> : nullptr;
+  switch (mode) {
+    case kModePlain: return chunk_fwd_bf16_kernel<kCT, kModePlain, kGateChannel, false>;
+    case kModeEmit: return chunk_fwd_bf16_kernel<kCT, kModeEmit, kGateChannel, false>;
+    case kModePacked: return chunk_fwd_bf16_kernel<kCT, kModePacked, kGateChannel, false>;
+    case kModeFragment: return chunk_fwd_bf16_kernel<kCT, kModeFragment, kGateChannel, false>;
+    case kModeTransition: return chunk_fwd_bf16_kernel<kCT, kModeTransition, kGateChannel, false>;
+  }
+  return nullptr;
+}
+
+}  // namespace
+
 hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, const void* a, const float* beta,
                                  const float* initial_state, void* o, float* final_state, int B, int T, int H,
-                                 hipStream_t stream, float* states, int state_every, int n_states,
-                                 const int* cu_seqlens) {
-  const int units = B * H;
+                                 hipStream_t stream, const PrefillOptions& opt) {
+  // B counts the kernel's sequences: with segments, B sequences of T tokens
+  // each make B * seg_count of them
+  const int seqs = opt.seg_len > 0 ? B * opt.seg_count : B;
+  const int units = seqs * H;
   if (units == 0) return hipSuccess;
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;
+  const bool norm = opt.z != nullptr;
+  PrefillKernel k_pairs = pick_kernel<1>(opt.mode, opt.gate, norm);
+  PrefillKernel k_single = pick_kernel<2>(opt.mode, opt.gate, norm);
+  if (!k_single) return hipErrorInvalidValue;  // not instantiated: the API checks never ask for one
   auto launch = [&](bool pairs, int u0, int u1) {
     const unsigned grid = pairs ? (unsigned)(16 * (((int64_t)(u1 - u0) + 7) / 8)) : (unsigned)(u1 - u0);
-    // checkpoints and packed sequences are not requested together
-    auto kernel = pairs ? (states ? chunk_fwd_bf16_kernel<1, true, false>
-                                  : cu_seqlens ? chunk_fwd_bf16_kernel<1, false, true> : chunk_fwd_bf16_kernel<1, false, false>)
-                        : (states ? chunk_fwd_bf16_kernel<2, true, false>
-                                  : cu_seqlens ? chunk_fwd_bf16_kernel<2, false, true> : chunk_fwd_bf16_kernel<2, false, false>);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                       (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T, H, u0, u1, states, state_every,
-                       n_states, cu_seqlens);
+    hipLaunchKernelGGL(pairs ? k_pairs : k_single, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
+                       H, u0, u1, opt.states, opt.state_every, opt.n_states, opt.cu_seqlens, opt.seg_len,
+                       opt.seg_count, opt.last_only ? 1 : 0, (const bf16*)opt.z, opt.eps);
   };
   // Sequences that fit on the device at once as two workgroups each (one per
-  // compute unit, whole groups of 8).
-  const int pair_units = 8 * (cus / 16);
+  // compute unit, whole groups of 8); the fused norm needs a whole row of O
+  // in one workgroup, so it always runs one workgroup per sequence.
+  const int pair_units = k_pairs ? 8 * (cus / 16) : 0;
   if (units <= pair_units) {
     launch(true, 0, units);
   } else if (units <= cus) {

@@ -12,10 +12,8 @@
  *   before the delta correction, as the reference step in that section fixes.
  *   S has Dk rows (key channels) and Dv columns (value channels).
  *   The learned scale e^A of eq. (5) is folded into a by the caller.
- *   The family's other rules run through the same entry points: a = -inf
- *   (sigmoid 0, so alpha = 1) gives the plain delta rule, and one logit per
- *   token and head repeated over the channels gives a scalar-gated delta
- *   rule with the same bounded gate.
+ *   The family's other rules (the delta rule, alpha = 1, and the
+ *   scalar-gated delta rule) have entry points of their own (kda_gate).
  *
  * Conventions for every entry point:
  *   - Every pointer is a device pointer (hipMalloc'd or equivalent), row-major,
@@ -40,6 +38,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -57,6 +56,23 @@ typedef enum {
   KDA_F32 = 0,  /* q, k, v, a, o are fp32 */
   KDA_BF16 = 1  /* q, k, v, a, o are bf16; beta and states stay fp32 */
 } kda_dtype;
+
+/*
+ * The gate of the *_gated entry points: the members of the family of update
+ * rules the notebook "Kimi K3: Two point eight trillion parameters, open
+ * weights, and forty-seven pages of how" compares (section "The sequence
+ * axis"), all through the bounded gate g = -5 sigmoid(a) of eq. (5):
+ *   KDA_GATE_CHANNEL  a has one logit per key channel ([.., Dk] in the I/O
+ *                     dtype, 16-byte aligned): KDA, as in the plain entries;
+ *   KDA_GATE_SCALAR   a has one fp32 logit per token and head ([..] shaped
+ *                     like beta, 4-byte aligned): the scalar-gated delta rule;
+ *   KDA_GATE_NONE     alpha = 1, a is not read (may be NULL): the delta rule.
+ */
+typedef enum {
+  KDA_GATE_CHANNEL = 0,
+  KDA_GATE_SCALAR = 1,
+  KDA_GATE_NONE = 2
+} kda_gate;
 
 /*
  * Chunkwise prefill: T tokens of B independent sequences, H heads each.
@@ -84,6 +100,38 @@ typedef enum {
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* a, const float* beta,
                          const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
                          int Dv, kda_dtype dtype, void* hip_stream);
+
+/*
+ * kda_chunk_fwd with a choice of gate (kda_gate above): the gate logits a are
+ * [B, T, H, Dk] in dtype (KDA_GATE_CHANNEL), [B, T, H] fp32 (KDA_GATE_SCALAR),
+ * or not read (KDA_GATE_NONE).  Every other argument and result is as in
+ * kda_chunk_fwd, which is this call with KDA_GATE_CHANNEL.  A bad gate
+ * value returns KDA_ERR_INVALID_ARGUMENT.
+ */
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                               const float* initial_state, void* o, float* final_state, int B, int T, int H, int Dk,
+                               int Dv, kda_dtype dtype, kda_gate gate, void* hip_stream);
+
+/*
+ * kda_chunk_fwd followed by the output side of eq. (6) of the page "Kimi
+ * K3：从三条信息流到完整系统" without its projections, fused into the
+ * prefill's output store for bf16 I/O: instead of o the call writes
+ *
+ *   y = sigmoid(z) * o / sqrt(mean(o^2) + eps)     per (token, head) row of Dv channels,
+ *
+ * the head-wise RMSNorm (no learned scale) of the recurrent output, gated by
+ * z = W_g x from the caller.  o itself is never written to memory.
+ *
+ *   z   [B, T, H, Dv]  dtype  (read)
+ *   y   [B, T, H, Dv]  dtype  (written)
+ *
+ * The norm is taken of o rounded to dtype, as kda_output_gate_norm would
+ * read it.  With fp32 I/O the norm runs as a second pass over y.  Every
+ * other argument is as in kda_chunk_fwd; eps must be finite and >= 0.
+ */
+kda_status kda_chunk_fwd_norm(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                              const float* initial_state, const void* z, float eps, void* y, float* final_state, int B,
+                              int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream);
 
 /*
  * kda_chunk_fwd that also writes state checkpoints: the state after tokens
@@ -135,6 +183,40 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream);
 
 /*
+ * kda_chunk_fwd with each sequence cut into segments that run side by side:
+ * the page "Kimi K3：从三条信息流到完整系统", section "FlashKDA 与 KCP",
+ * eq. (17), on one device.  A segment acts on the state it enters with as
+ * S -> M S + E (eq. (1) is affine in S): the library runs every segment but
+ * the last of each sequence from S = I with v = 0 (its transition M) and
+ * from zero (its fragment E), composes the entering states
+ * S_in[j + 1] = M_j S_in[j] + E_j from S_in[0] = initial_state, and runs all
+ * segments again from those, writing o and the final states.  Three passes
+ * of the state path for `segments` times the (sequence, head) parallelism:
+ * worth it when B * H leaves most compute units idle.
+ *
+ * Segments are whole 16-token chunks: L = ceil(ceil(T / segments) / 16) * 16
+ * tokens each, ceil(T / L) of them (the last takes the rest).  Arguments and
+ * results are those of kda_chunk_fwd (up to rounding: the composition adds
+ * fp32 products of the segments' states), plus
+ *
+ *   segments         >= 1; 1 (or T <= 16) runs kda_chunk_fwd itself
+ *   workspace        device memory of at least kda_chunk_fwd_split_workspace
+ *                    (B, T, H, segments) bytes, 16-byte aligned, owned by the
+ *                    caller; its contents on entry do not matter and it must
+ *                    not overlap any other argument; may be NULL when that
+ *                    size is 0
+ *   workspace_bytes  its size; a smaller one returns KDA_ERR_INVALID_ARGUMENT
+ *
+ * initial_state may be final_state (it is read before final_state is
+ * written).  Only the per-channel gate (kda_chunk_fwd's a) is taken.
+ */
+size_t kda_chunk_fwd_split_workspace(int B, int T, int H, int segments);
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                               const float* initial_state, void* o, float* final_state, int segments,
+                               void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv,
+                               kda_dtype dtype, void* hip_stream);
+
+/*
  * One recurrent decode step: eq. (1) applied to a single token of each of B
  * sequences and H heads, updating the state in place (read once, written
  * once).
@@ -148,6 +230,13 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,
                            float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype,
                            void* hip_stream);
+
+/* kda_decode_step with a choice of gate: a is [B, H, Dk] in dtype
+ * (KDA_GATE_CHANNEL), [B, H] fp32 (KDA_GATE_SCALAR) or not read
+ * (KDA_GATE_NONE). */
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                 float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, kda_gate gate,
+                                 void* hip_stream);
 
 /*
  * K tokens of each sequence in one pass, for speculative decoding: the state
@@ -184,6 +273,13 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
 kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
                             kda_dtype dtype, void* hip_stream);
+
+/* kda_decode_multi with a choice of gate: a is [B, K, H, Dk] in dtype
+ * (KDA_GATE_CHANNEL), [B, K, H] fp32 (KDA_GATE_SCALAR) or not read
+ * (KDA_GATE_NONE). */
+kda_status kda_decode_multi_gated(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                  float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,
+                                  kda_dtype dtype, kda_gate gate, void* hip_stream);
 
 /*
  * The output side of eq. (6) of the page "Kimi K3：从三条信息流到完整系统"

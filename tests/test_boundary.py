@@ -28,7 +28,9 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_chunk_fwd_states", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_decode_multi",
-              "kda_output_gate_norm", "kda_compose_segments", "kda_status_string", "kda_last_error", "kda_version"):
+              "kda_output_gate_norm", "kda_compose_segments", "kda_status_string", "kda_last_error", "kda_version",
+              "kda_chunk_fwd_gated", "kda_chunk_fwd_norm", "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace",
+              "kda_decode_step_gated", "kda_decode_multi_gated"):
         assert n in names
 
 
@@ -307,3 +309,122 @@ def test_binding_raises_without_the_library(monkeypatch):
         kda.lib()
     with pytest.raises(RuntimeError, match="no fallback"):
         kda.last_error()
+
+
+# --------------------------------------------------------------------------- gate modes, fused norm, split
+
+
+def gated(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, initial_state=None, o=P, final_state=P, B=1, T=16, H=1, Dk=128, Dv=128,
+                dtype=kda.KDA_BF16, gate=kda.KDA_GATE_CHANNEL)
+    args.update(kw)
+    return kda.raw_chunk_fwd_gated(*args.values())
+
+
+def test_gate_argument_checks(lib):
+    assert gated(gate=3) == kda.KDA_ERR_INVALID_ARGUMENT and "gate" in kda.last_error()
+    assert gated(gate=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    # channel logits are rows like q: 16-byte aligned; the scalar logits are fp32 like beta: 4-byte aligned
+    assert gated(a=MIS) == kda.KDA_ERR_INVALID_ARGUMENT and "aligned" in kda.last_error()
+    assert gated(a=None) == kda.KDA_ERR_INVALID_ARGUMENT and "a is NULL" in kda.last_error()
+    assert gated(a=None, gate=kda.KDA_GATE_SCALAR) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert gated(a=P + 2, gate=kda.KDA_GATE_SCALAR) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert gated(q=None, gate=kda.KDA_GATE_NONE) == kda.KDA_ERR_INVALID_ARGUMENT  # the other checks still run
+    assert gated(Dk=64, gate=kda.KDA_GATE_NONE) == kda.KDA_ERR_UNSUPPORTED
+    for entry, args in ((kda.raw_decode_step_gated, (P, P, P, P, P, P, P, 1, 1, 128, 128, kda.KDA_BF16, 7)),
+                        (kda.raw_decode_multi_gated, (P, P, P, P, P, P, P, None, 1, 2, 1, 128, 128, kda.KDA_BF16, 7))):
+        assert entry(*args) == kda.KDA_ERR_INVALID_ARGUMENT and "gate" in kda.last_error()
+    assert kda.raw_decode_step_gated(P, P, P, None, P, P, P, 1, 1, 128, 128, kda.KDA_BF16,
+                                     kda.KDA_GATE_SCALAR) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert kda.raw_decode_multi_gated(P, P, P, P + 4, P, P, P, None, 1, 2, 1, 128, 128, kda.KDA_BF16,
+                                      kda.KDA_GATE_CHANNEL) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_fused_norm_argument_checks(lib):
+    def call(**kw):
+        args = dict(q=P, k=P, v=P, a=P, beta=P, initial_state=None, z=P, eps=1e-6, y=P, final_state=P, B=1, T=16,
+                    H=1, Dk=128, Dv=128, dtype=kda.KDA_BF16)
+        args.update(kw)
+        return kda.raw_chunk_fwd_norm(*args.values())
+
+    assert call(z=None) == kda.KDA_ERR_INVALID_ARGUMENT and "z" in kda.last_error()
+    assert call(z=MIS) == kda.KDA_ERR_INVALID_ARGUMENT and "aligned" in kda.last_error()
+    assert call(y=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(eps=-1.0) == kda.KDA_ERR_INVALID_ARGUMENT and "eps" in kda.last_error()
+    assert call(eps=float("inf")) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(Dv=64) == kda.KDA_ERR_UNSUPPORTED
+
+
+def split(**kw):
+    args = dict(q=P, k=P, v=P, a=P, beta=P, initial_state=None, o=P, final_state=P, segments=4, workspace=P,
+                workspace_bytes=1 << 40, B=1, T=4096, H=2, Dk=128, Dv=128, dtype=kda.KDA_BF16)
+    args.update(kw)
+    return kda.raw_chunk_fwd_split(*args.values())
+
+
+def test_split_workspace_size(lib):
+    state = 128 * 128 * 4
+    # 4096 tokens in 4 segments of 1024: 3 transitions, 3 fragments and 4 entering states per (b, h)
+    assert kda.kda_chunk_fwd_split_workspace(1, 4096, 2, 4) == 2 * state * (3 + 3 + 4)
+    # 4100 tokens in 16 segments: segments of 272 tokens (whole chunks), 16 of them (the last one 20 tokens)
+    assert kda.kda_chunk_fwd_split_workspace(2, 4100, 9, 16) == 2 * 9 * state * (15 + 15 + 16)
+    # segments of whole chunks: 100 tokens in 8 segments are 7 segments of 16
+    assert kda.kda_chunk_fwd_split_workspace(1, 100, 1, 8) == state * (6 + 6 + 7)
+    for args in ((1, 4096, 2, 1), (1, 16, 2, 8), (0, 4096, 2, 4), (1, 0, 2, 4), (1, 4096, 0, 4)):
+        assert kda.kda_chunk_fwd_split_workspace(*args) == 0, args
+
+
+def test_split_argument_checks(lib):
+    need = kda.kda_chunk_fwd_split_workspace(1, 4096, 2, 4)
+    assert split(workspace_bytes=need - 1) == kda.KDA_ERR_INVALID_ARGUMENT and "workspace" in kda.last_error()
+    assert split(workspace=None) == kda.KDA_ERR_INVALID_ARGUMENT and "workspace" in kda.last_error()
+    assert split(workspace=MIS) == kda.KDA_ERR_INVALID_ARGUMENT and "aligned" in kda.last_error()
+    assert split(segments=0) == kda.KDA_ERR_INVALID_ARGUMENT and "segments" in kda.last_error()
+    for field in ("q", "k", "v", "a", "beta", "o", "final_state"):
+        assert split(**{field: None}) == kda.KDA_ERR_INVALID_ARGUMENT, field
+        assert split(**{field: MIS}) == kda.KDA_ERR_INVALID_ARGUMENT, field
+    assert split(initial_state=MIS) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert split(Dk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert split(H=65537) == kda.KDA_ERR_UNSUPPORTED
+    assert split(T=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert split(B=1 << 20, H=1 << 8, segments=16) == kda.KDA_ERR_INVALID_ARGUMENT  # B*H*segments over the limit
+    assert split(dtype=9) == kda.KDA_ERR_INVALID_ARGUMENT
+    # one segment (or a short sequence) is the plain prefill and needs no workspace: checks only, B = 0 is a no-op
+    assert split(segments=1, workspace=None, workspace_bytes=0, q=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert split(B=0, workspace=None, workspace_bytes=0) == kda.KDA_OK
+
+
+def _relaxed_require(t, name, shape, dtype, device):
+    """The binding's argument check without the device test, so that the
+    order of its checks can be seen with host tensors."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def test_split_binding_checks_outputs_before_any_call(lib, monkeypatch):
+    """A non-contiguous o or a final_state of the wrong dtype is rejected by
+    the split binding itself (a reshape would have written into a copy)."""
+    torch = pytest.importorskip("torch")
+    monkeypatch.setattr(kda, "_require", _relaxed_require)
+    calls = []
+    monkeypatch.setattr(kda, "_check", lambda status: calls.append(status))
+    B, T, H, D = 1, 64, 2, 128
+    x = {n: torch.zeros(B, T, H, D, dtype=torch.bfloat16) for n in ("q", "k", "v", "a")}
+    beta = torch.zeros(B, T, H)
+    o_t = torch.zeros(B, H, T, D, dtype=torch.bfloat16).transpose(1, 2)  # [B, T, H, D] view, not contiguous
+    with pytest.raises(ValueError, match="o must be contiguous"):
+        kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], beta, 2, o=o_t)
+    with pytest.raises(TypeError, match="final_state"):
+        kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], beta, 2,
+                                final_state=torch.zeros(B, H, D, D, dtype=torch.float64))
+    with pytest.raises(ValueError, match="initial_state"):
+        kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], beta, 2, initial_state=torch.zeros(B, H, D, 64))
+    with pytest.raises(ValueError, match="workspace holds"):
+        kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], beta, 2, workspace=torch.zeros(16, dtype=torch.uint8))
+    assert calls == []  # nothing reached the library

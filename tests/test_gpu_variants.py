@@ -1,0 +1,244 @@
+"""GPU parity of the gate modes, the fused output gate and norm, and the
+sequence split, through the C ABI, against the fp64 oracle.
+
+- Gate modes (the family of update rules the notebook compares in its
+  section "The sequence axis"): one fp32 logit per token and head (the
+  scalar-gated delta rule) and no gate (alpha = 1, the delta rule), checked
+  against the oracle's log-decay path with g given directly (the scalar gate
+  repeated over the key channels, or zeros).
+- The fused epilogue: y = sigmoid(z) * RMSNorm(o) (eq. (6) of the K3 page
+  without its projections) against the oracle's output_gate_norm of the
+  oracle's own o.
+- The split (section "FlashKDA 与 KCP", eq. (17)): segments of 256 to 4,096
+  tokens, in both launch layouts, against the oracle and against the
+  unsplit prefill, including the benchmark's shape (8 heads x 65,536 tokens
+  in 16 segments) and a call on a side stream."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.conftest import gpu_available
+from tests.gpu_common import TOL, WORKLOADS, device_inputs, host_inputs, oracle_block, print_case, rel_l2, to_np, variant
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_23_amd as kda_mod
+
+    kda_mod.lib()
+    return kda_mod
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    import gc
+
+    import torch
+
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def per_block_worst(x, ref, axes):
+    num = np.sqrt(((x - ref) ** 2).sum(axis=axes))
+    den = np.sqrt((ref ** 2).sum(axis=axes))
+    return float((num / np.maximum(den, 1e-300)).max())
+
+
+# --------------------------------------------------------------------------- gate modes
+
+
+def _gate_inputs(w, B, T, H, mode):
+    """Device inputs with the gate of `mode`, and the oracle's log-decays g
+    [B, T, H, 128] for them (from the scalar logits as the device holds them)."""
+    import torch
+
+    x = device_inputs(w, B=B, T=T, H=H)
+    h = host_inputs(w, nb=B, nt=T, nh=H)
+    if mode == "scalar":
+        # one logit per token and head: N(0, 1) from the first channel of a, as fp32
+        a_dev = x["a"][..., 0].float().contiguous()
+        g = np.repeat(oracle.gate(synth.to_f64(h["a"])[..., :1]), 128, axis=3)
+    else:
+        a_dev = None
+        g = np.zeros((B, T, H, 128))
+    return x, h, a_dev, g
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["scalar", "none"])
+@pytest.mark.parametrize("shape", [(2, 3, 37), (1, 4, 700), (3, 97, 200)], ids=lambda s: "B%dH%dT%d" % s)
+def test_prefill_gate_modes(kda, dtype, mode, shape):
+    """Ragged short, steady-state (44 chunks) and 291-sequence (single
+    workgroups, then pairs) prefills with either gate mode."""
+    B, H, T = shape
+    if dtype == "f32" and H == 97:
+        pytest.skip("the fp32 prefill has one layout")
+    w = variant(WORKLOADS[2], index=300 + T, dtype=dtype)
+    print_case(f"case prefill gate {mode} {dtype} B={B} H={H} T={T}")
+    x, h, a_dev, g = _gate_inputs(w, B, T, H, mode)
+    o, S = kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], a_dev, x["beta"], gate=mode, initial_state=x["s0"])
+    import torch
+
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]),
+                                  h["beta"].astype(np.float64), g=g, s0=h["s0"].astype(np.float64))
+    wo, ws = per_block_worst(to_np(o), o_ref, (1, 3)), per_block_worst(to_np(S), S_ref, (2, 3))
+    print_case(f"  worst per-sequence rel_l2 o={wo:.2e} S={ws:.2e}")
+    assert wo <= TOL[dtype] and ws <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["scalar", "none", "channel"])
+def test_decode_gate_modes(kda, dtype, mode):
+    """Eight single steps and one eight-token multi-token call (commit counts
+    8, 0, 5) with each gate mode, against the oracle."""
+    import torch
+
+    w = variant(WORKLOADS[4], index=320, dtype=dtype)
+    B, K, H = 3, 8, 5
+    x, h, a_dev, g = _gate_inputs(w, B, K, H, mode if mode != "channel" else "none")
+    if mode == "channel":
+        a_dev = x["a"]
+        g = oracle.gate(synth.to_f64(h["a"]))
+    s0 = h["s0"].astype(np.float64)
+    state = x["s0"].clone()
+    outs = []
+    for t in range(K):
+        at = None if a_dev is None else a_dev[:, t].contiguous()
+        outs.append(kda.kda_decode_step_gated(*(x[n][:, t].contiguous() for n in ("q", "k", "v")), at,
+                                              x["beta"][:, t].contiguous(), state, gate=mode))
+    counts = [K, 0, 5]
+    state_m = x["s0"].clone()
+    om = kda.kda_decode_multi_gated(x["q"], x["k"], x["v"], a_dev, x["beta"], state_m, gate=mode,
+                                    n_commit=torch.tensor(counts, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    q, k, v = (synth.to_f64(h[n]) for n in ("q", "k", "v"))
+    beta = h["beta"].astype(np.float64)
+    o_ref, S_ref = oracle.forward(q, k, v, beta, g=g, s0=s0)
+    om_ref, Sm_ref = oracle.decode_multi(q, k, v, beta, s0, g=g, n_commit=counts)
+    e = [rel_l2(to_np(torch.stack(outs, dim=1)), o_ref), rel_l2(to_np(state), S_ref),
+         rel_l2(to_np(om), om_ref), rel_l2(to_np(state_m), Sm_ref)]
+    print_case(f"  decode gate {mode} {dtype}: rel_l2 step o/S, multi o/S = " + " ".join(f"{v:.2e}" for v in e))
+    assert max(e) <= TOL[dtype]
+
+
+def test_gate_channel_mode_is_kda_chunk_fwd(kda):
+    """The gated entry with the per-channel gate is kda_chunk_fwd, bit for bit."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=330)
+    x = device_inputs(w, B=1, T=300, H=4)
+    o1, S1 = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"])
+    o2, S2 = kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["a"], x["beta"], gate="channel",
+                                     initial_state=x["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+# --------------------------------------------------------------------------- fused output gate and norm
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 3, 37), (1, 8, 1000), (3, 97, 100)], ids=lambda s: "B%dH%dT%d" % s)
+def test_fused_norm_against_oracle(kda, dtype, shape):
+    """y = sigmoid(z) * RMSNorm(o) from the fused prefill (a zero z row and a
+    saturated one included):
+    - end to end, against the oracle's norm of the oracle's o, pooled over
+      the tensor (the norm rescales every row to unit RMS, so a row whose o
+      is small after cancellation carries its whole relative error into y:
+      a per-row or per-sequence figure measures that conditioning, not the
+      kernels);
+    - the epilogue, against the oracle's norm of the prefill's own o from
+      kda_chunk_fwd (rounding of o and y only);
+    - the final state against kda_chunk_fwd's (the fused call runs one
+      workgroup per sequence, the plain one may run pairs: rounding only)."""
+    import torch
+
+    B, H, T = shape
+    if dtype == "f32" and H == 97:
+        pytest.skip("the fp32 prefill has one layout")
+    w = variant(WORKLOADS[2], index=340 + T, dtype=dtype)
+    print_case(f"case fused norm {dtype} B={B} H={H} T={T}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    z = (x["v"].float() * 3.0).to(x["v"].dtype).contiguous()  # any gate pre-activation, several magnitudes
+    z[0, 0] = 0
+    z[0, min(1, T - 1), 0] = -80.0
+    y, S = kda.kda_chunk_fwd_norm(x["q"], x["k"], x["v"], x["a"], x["beta"], z, eps=1e-6, initial_state=x["s0"])
+    o1, S1 = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"])
+    torch.cuda.synchronize()
+    o_ref, _ = oracle_block(w, nb=B, nt=T, nh=H)
+    zf = to_np(z)
+    y_ref = oracle.output_gate_norm(o_ref, zf, 1e-6)
+    y_own = oracle.output_gate_norm(to_np(o1), zf, 1e-6)
+    e_end, e_epi, e_state = rel_l2(to_np(y), y_ref), rel_l2(to_np(y), y_own), rel_l2(to_np(S), to_np(S1))
+    print_case(f"  rel_l2 y vs oracle {e_end:.2e}; vs the norm of the prefill's o {e_epi:.2e}; state {e_state:.2e}")
+    assert e_end <= TOL[dtype]
+    assert e_epi <= (1e-6 if dtype == "f32" else 1e-2)
+    assert e_state <= 1e-6
+
+
+# --------------------------------------------------------------------------- the split
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,T,P", [(1, 4, 4096, 4), (1, 8, 8192, 16), (2, 9, 4100, 16)],
+                         ids=["H4T4096P4", "H8T8192P16", "B2H9T4100P16"])
+def test_split_through_the_abi(kda, dtype, B, H, T, P):
+    """kda_chunk_fwd_split against the oracle and the unsplit prefill:
+    segments of 1,024, 512 and 272 tokens (the last one ragged); 2 x 9 x 16 =
+    288 segment-heads run 256 single workgroups and then pairs."""
+    import torch
+
+    if dtype == "f32" and B == 2:
+        pytest.skip("the fp32 prefill has one layout")
+    w = variant(WORKLOADS[2], index=350 + P + H, dtype=dtype, s0_scale=0.3)
+    print_case(f"case split abi {dtype} B={B} H={H} T={T} P={P}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, S = kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], x["beta"], P, initial_state=x["s0"])
+    o1, S1 = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_block(w, nb=B, nt=T, nh=H)
+    e = [per_block_worst(to_np(o), o_ref, (1, 3)), per_block_worst(to_np(S), S_ref, (2, 3)),
+         rel_l2(to_np(o), to_np(o1)), rel_l2(to_np(S), to_np(S1))]
+    print_case("  worst rel_l2 o/S vs oracle, pooled vs kda_chunk_fwd: " + " ".join(f"{v:.2e}" for v in e))
+    assert max(e) <= TOL[dtype]
+
+
+def test_split_benchmark_shape(kda):
+    """The shape bench.py times: 8 heads x 65,536 tokens in 16 segments of
+    4,096 tokens (bf16, no initial state), every head against the oracle."""
+    import torch
+
+    w = variant(WORKLOADS[1], index=360)
+    B, H, T, P = 1, 8, 65536, 16
+    print_case(f"case split bench shape B={B} H={H} T={T} P={P}")
+    x = device_inputs(w, B=B, T=T, H=H)
+    o, S = kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], x["beta"], P)
+    o1, S1 = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_block(w, nb=B, nt=T, nh=H)
+    e = [per_block_worst(to_np(o), o_ref, (1, 3)), per_block_worst(to_np(S), S_ref, (2, 3)),
+         rel_l2(to_np(o), to_np(o1)), rel_l2(to_np(S), to_np(S1))]
+    print_case("  worst rel_l2 o/S vs oracle, pooled vs kda_chunk_fwd: " + " ".join(f"{v:.2e}" for v in e))
+    assert max(e) <= TOL["bf16"]
+
+
+def test_split_on_a_side_stream(kda):
+    """A call with stream=side from the default stream (the workspace and
+    outputs allocated on that stream) gives the default-stream call's bits."""
+    import torch
+
+    w = variant(WORKLOADS[2], index=361)
+    x = device_inputs(w, B=1, T=2048, H=4)
+    o_ref, S_ref = kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], x["beta"], 8, initial_state=x["s0"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o, S = kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], x["beta"], 8, initial_state=x["s0"], stream=side)
+    side.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
