@@ -82,6 +82,8 @@ def lib():
         L.kda_chunk_fwd_split_workspace.restype = ctypes.c_size_t
         L.kda_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i, p, ctypes.c_size_t, i, i, i, i, i, i, p]
         L.kda_chunk_fwd_split.restype = i
+        L.kda_chunk_fwd_split_noalloc.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, p]
+        L.kda_chunk_fwd_split_noalloc.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -561,6 +563,12 @@ def raw_chunk_fwd_split(q, k, v, a, beta, initial_state, o, final_state, segment
                         H, Dk, Dv, dtype, stream=0):
     return lib().kda_chunk_fwd_split(q, k, v, a, beta, initial_state, o, final_state, segments, workspace,
                                      workspace_bytes, B, T, H, Dk, Dv, dtype, stream)
+
+
+def raw_chunk_fwd_split_noalloc(q, k, v, a, beta, initial_state, o, final_state, segments, B, T, H, Dk, Dv, dtype,
+                                stream=0):
+    return lib().kda_chunk_fwd_split_noalloc(q, k, v, a, beta, initial_state, o, final_state, segments, B, T, H, Dk,
+                                             Dv, dtype, stream)
 
 
 def raw_decode_step_gated(q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, gate, stream=0):

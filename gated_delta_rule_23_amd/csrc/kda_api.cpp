@@ -305,6 +305,33 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
   return ok();
 }
 
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                       const float* initial_state, void* o, float* final_state, int segments, int B,
+                                       int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
+  static const char* fn = "kda_chunk_fwd_split_noalloc";
+  if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: segments=%d must be at least 1", fn, segments);
+  KDA_TRY(check_common(fn, B, H, Dk, Dv, dtype));
+  if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative size (T=%d)", fn, T);
+  int P = 1, L = 0;
+  split_shape(T, segments, &P, &L);
+  if ((int64_t)B * H * P > kMaxUnits)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H*segments exceeds the limit of %lld sequences", fn,
+                (long long)kMaxUnits);
+  const size_t need = kda::split_workspace_bytes(B, P, H);
+  if (need > kda::kSplitScratchBytes)
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "%s: the split needs %zu bytes of scratch (B*H = %lld, %d segments), more than the %zu bytes the "
+                "library holds; use fewer segments or kda_chunk_fwd_split with a workspace",
+                fn, need, (long long)B * H, P, kda::kSplitScratchBytes);
+  void* work = nullptr;  // the device address of the library's scratch array
+  if (need > 0 && (int64_t)B * H > 0 && T > 0) {
+    const hipError_t e = kda::split_noalloc_scratch(static_cast<hipStream_t>(hip_stream), &work);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
+  }
+  return kda_chunk_fwd_split(q, k, v, a, beta, initial_state, o, final_state, segments, work, need, B, T, H, Dk, Dv,
+                             dtype, hip_stream);
+}
+
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* a, const float* beta,
                            float* state, void* o, int B, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream) {
   return decode_impl("kda_decode_step", q, k, v, a, beta, state, o, B, H, Dk, Dv, dtype, KDA_GATE_CHANNEL, hip_stream);

@@ -85,4 +85,8 @@ size_t split_workspace_bytes(int B, int P, int H);
 hipError_t launch_split(const void* q, const void* k, const void* v, const void* a, const float* beta,
                         const float* initial_state, void* o, float* final_state, int B, int T, int H, int P,
                         int seg_len, bool bf16_io, void* workspace, hipStream_t stream);
+/* The file-scope scratch of kda_chunk_fwd_split_noalloc on the stream's
+ * device (its device address, looked up once per device) and its size. */
+hipError_t split_noalloc_scratch(hipStream_t stream, void** ptr);
+extern const size_t kSplitScratchBytes;
 }  // namespace kda

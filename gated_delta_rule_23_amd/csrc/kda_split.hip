@@ -22,10 +22,53 @@
  * path instead of one, for P times the (sequence, head) parallelism.  The
  * caller's workspace holds M, E and S_in.
  */
+#include <mutex>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
+
+namespace {
+
+/* The workspace of kda_chunk_fwd_split_noalloc: a file-scope device array,
+ * allocated with the library's code object on every GPU it runs on and held
+ * until the process ends.  Host code never uses its name as an address: the
+ * device address comes from hipGetSymbolAddress, once per device, and is
+ * kept in scratch_ptr. */
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+const size_t kSplitScratchBytes = kScratchBytes;
+
+hipError_t split_noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    // with the stream's device current: each device holds its own copy of the array
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t split_workspace_bytes(int B, int P, int H) {
   if (P <= 1) return 0;

@@ -217,6 +217,23 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                                kda_dtype dtype, void* hip_stream);
 
 /*
+ * kda_chunk_fwd_split for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with the workspace taken
+ * from a scratch array the library holds on every GPU it runs on (64 MiB
+ * each, kept until the process ends).  Nothing is allocated and nothing
+ * needs to start at zero.  A split needing more than 64 MiB
+ * (kda_chunk_fwd_split_workspace above: 192 KiB per (sequence, head,
+ * segment), e.g. 8 heads x 16 segments = 23 MiB) returns
+ * KDA_ERR_INVALID_ARGUMENT.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race on it and must be ordered by the caller.
+ */
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const void* a, const float* beta,
+                                       const float* initial_state, void* o, float* final_state, int segments, int B,
+                                       int T, int H, int Dk, int Dv, kda_dtype dtype, void* hip_stream);
+
+/*
  * One recurrent decode step: eq. (1) applied to a single token of each of B
  * sequences and H heads, updating the state in place (read once, written
  * once).

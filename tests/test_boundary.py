@@ -428,3 +428,19 @@ def test_split_binding_checks_outputs_before_any_call(lib, monkeypatch):
     with pytest.raises(ValueError, match="workspace holds"):
         kda.kda_chunk_fwd_split(x["q"], x["k"], x["v"], x["a"], beta, 2, workspace=torch.zeros(16, dtype=torch.uint8))
     assert calls == []  # nothing reached the library
+
+
+def test_noalloc_split_checks(lib):
+    """The no-allocation split checks its arguments and its scratch limit
+    (64 MiB) before it touches the device."""
+    def call(**kw):
+        args = dict(q=P, k=P, v=P, a=P, beta=P, initial_state=None, o=P, final_state=P, segments=16, B=1, T=8192,
+                    H=8, Dk=128, Dv=128, dtype=kda.KDA_BF16)
+        args.update(kw)
+        return kda.raw_chunk_fwd_split_noalloc(*args.values())
+
+    assert call(H=96) == kda.KDA_ERR_INVALID_ARGUMENT and "scratch" in kda.last_error()  # 276 MiB needed
+    assert call(segments=0) == kda.KDA_ERR_INVALID_ARGUMENT and "segments" in kda.last_error()
+    assert call(Dk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert call(T=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(B=0) == kda.KDA_OK
