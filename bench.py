@@ -12,11 +12,14 @@ rates measured on the same box (a device copy and MFMA loops), and every
 fraction is also given against those; `decode` adds kda_decode_step on the
 decode workload (256 sequences x 96 heads, fp32 state updated in place, 64
 steps with fresh inputs); `decode_multi` takes the same 64 tokens per state
-four at a time through kda_decode_multi; `cpu_baseline` is the fp64 oracle
-timed on the host on the default workload, with stated samples of the others.
+four at a time through kda_decode_multi; `gate_modes` the prefill with a
+scalar gate and with none, `fused_norm` the prefill with the output gate and
+norm fused against two passes, `split` the sequence split against the plain
+prefill from 8 to 96 heads; `cpu_baseline` is the fp64 oracle timed on the
+host on the default workload, with stated samples of the others.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-configs] [--no-long]
-                    [--decode-tokens K] [--workload 0|1|2|3]   (the prefill workload of the main line)
+                    [--no-split] [--decode-tokens K] [--workload 0|1|2|3]   (the prefill workload of the main line)
 """
 import argparse
 import hashlib
@@ -190,7 +193,7 @@ def prefill_fields(pre, peaks_measured):
     fl = pre["launch_flops"] / avg_s
     mfma_peak = BF16_MFMA_PEAK if w.dtype == "bf16" else FP32_MFMA_PEAK
     mfma_meas = (peaks_measured or {}).get("mfma_bf16_tflops" if w.dtype == "bf16" else "mfma_f32_tflops")
-    hbm_meas = (peaks_measured or {}).get("hbm_copy_gbs")
+    hbm_meas = (peaks_measured or {}).get("hbm_gbs")
     roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
             "frac": achieved / HBM_PEAK, "frac_of_measured_peak": achieved / 1e9 / hbm_meas if hbm_meas else None,
             "kernel": PREFILL_KERNEL if w.dtype == "bf16" else "chunk_fwd_kernel", "launch_ms": pre["avg_ms"],
@@ -202,15 +205,24 @@ def prefill_fields(pre, peaks_measured):
 
 
 def measure_peaks():
-    """HBM copy and MFMA loop rates on this machine (peaks/)."""
+    """HBM and MFMA rates on this machine (peaks/): the best of a device copy and
+    a read pass (2 GiB, 16-byte non-temporal accesses, two workgroups of 256
+    threads per compute unit, the best of a sweep of 2 to 32), and the best of
+    loops of independent MFMAs of each bf16 shape (on gfx950 the 32x32x16
+    instruction reaches about twice the flop rate of the 16x16 ones)."""
     import peaks
 
-    return {"hbm_copy_gbs": peaks.hbm_copy() / 1e9, "mfma_bf16_tflops": peaks.mfma(bf16=True) / 1e12,
+    copy = peaks.hbm_copy(blocks_per_cu=2) / 1e9
+    read = peaks.hbm_read(blocks_per_cu=2) / 1e9
+    bf16 = {"16x16x32": peaks.mfma(bf16=True) / 1e12, "16x16x16": peaks.mfma(bf16=True, k16=True) / 1e12,
+            "32x32x16": peaks.mfma(bf16=True, shape32=True) / 1e12}
+    return {"hbm_copy_gbs": copy, "hbm_read_gbs": read, "hbm_gbs": max(copy, read),
+            "mfma_bf16_tflops": max(bf16.values()), "mfma_bf16_tflops_by_shape": bf16,
             "mfma_f32_tflops": peaks.mfma(bf16=False) / 1e12,
             "spec": {"hbm_gbs": HBM_PEAK / 1e9, "mfma_bf16_tflops": BF16_MFMA_PEAK / 1e12,
                      "mfma_f32_tflops": FP32_MFMA_PEAK / 1e12},
-            "how": "best of 5 launches of a 2 GiB device copy (16-byte non-temporal accesses; read + written "
-                   "bytes), and of loops of 8 independent 16x16x32 bf16 / 16x16x4 fp32 MFMAs on 4 waves per SIMD"}
+            "how": "best of 5 launches: 2 GiB copy (read + written bytes) and read; MFMA loops of 8 or 16 "
+                   "independent accumulators per wave, 4 waves per SIMD"}
 
 
 def bench_gate_norm(w, reps=50):
@@ -237,7 +249,85 @@ def bench_gate_norm(w, reps=50):
     return dict(rows=rows, avg_ms=sum(ms) / len(ms), bytes=3 * rows * D * 2)
 
 
-def bench_split(cases=((8, 65536, 16), (32, 32768, 8)), reps=10):
+# (H, T, segments) of single bf16 sequences: few heads (the split's use) up to the default workload's 96
+SPLIT_CASES = ((8, 65536, 16), (16, 65536, 8), (32, 32768, 8), (48, 32768, 4), (64, 32768, 4), (96, 8192, 2))
+
+
+def median_launch_ms(fn, stream, warm=10, reps=20):
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ms = sorted(timed_launches(fn, reps, stream))
+    return ms[len(ms) // 2]
+
+
+def bench_gate_modes(w):
+    """kda_chunk_fwd_gated on the default workload's shape with one fp32
+    logit per token and head ("scalar") and with no gate ("none"), against
+    the per-channel gate: median launch time and HBM rate (the gate's bytes
+    are 4 per token-head for the scalar gate, none without)."""
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+    from synth.workloads import device_inputs
+
+    x = device_inputs(w)
+    o = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((w.B, w.H, D, D), dtype=torch.float32, device="cuda")
+    a_scalar = x["a"][..., 0].float().contiguous()
+    stream = torch.cuda.current_stream()
+    out = {}
+    for mode, a, gate_bytes in (("channel", x["a"], 2 * D), ("scalar", a_scalar, 4), ("none", None, 0)):
+        ms = median_launch_ms(lambda: kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], a, x["beta"], gate=mode, o=o,
+                                                             final_state=S, stream=stream), stream)
+        nbytes = w.B * w.T * w.H * (BYTES_PER_TOKEN_HEAD_BF16 - 2 * D + gate_bytes) + w.B * w.H * STATE_BYTES
+        out[mode] = {"ms_per_launch": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+                     "gate_bytes_per_token_head": gate_bytes, "algorithmic_bytes_per_launch": nbytes,
+                     "hbm_frac": nbytes / (ms / 1e3) / HBM_PEAK}
+    del x, o, S, a_scalar
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_fused_norm(w):
+    """The prefill with sigmoid(z) * RMSNorm(o) fused into its output store
+    (kda_chunk_fwd_norm) against the prefill followed by the separate
+    kda_output_gate_norm pass, on the default workload's shape."""
+    import torch
+
+    import gated_delta_rule_23_amd as kda
+    from synth.workloads import device_inputs
+
+    x = device_inputs(w)
+    z = x["v"].clone()
+    o = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(o)
+    S = torch.empty((w.B, w.H, D, D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def two():
+        kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"], o=o, final_state=S,
+                          stream=stream)
+        kda.kda_output_gate_norm(o, z, 1e-6, y=y, stream=stream)
+
+    reps = 20 if w.T * w.B <= 8192 else 5
+    ms_fused = median_launch_ms(lambda: kda.kda_chunk_fwd_norm(x["q"], x["k"], x["v"], x["a"], x["beta"], z, eps=1e-6,
+                                                               initial_state=x["s0"], y=y, final_state=S,
+                                                               stream=stream), stream, warm=3, reps=reps)
+    ms_two = median_launch_ms(two, stream, warm=3, reps=reps)
+    # z read as well; the initial state when there is one
+    nbytes = (w.B * w.T * w.H * (BYTES_PER_TOKEN_HEAD_BF16 + 2 * D)
+              + w.B * w.H * STATE_BYTES * (2 if x["s0"] is not None else 1))
+    del x, z, o, y, S
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms_fused": ms_fused, "ms_prefill_then_norm": ms_two, "speedup": ms_two / ms_fused,
+            "algorithmic_bytes_fused": nbytes, "hbm_frac_fused": nbytes / (ms_fused / 1e3) / HBM_PEAK,
+            "layout": "one workgroup per sequence (a row's 128 value channels in one workgroup)"}
+
+
+def bench_split(cases=SPLIT_CASES, reps=10):
     """kda_chunk_fwd against kda_chunk_fwd_split on single sequences with
     few heads (B = 1; H, T, segments per case), bf16, median launch times."""
     import dataclasses
@@ -472,8 +562,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3],
                     help="prefill workload of the main line: 1 = B1 H96 T8192 (default), 0 = fp32 B1 H2 T512, "
                          "2 = B4 H96 T32768 with S0, 3 = B1 H96 T1048576 mixed decay")
-    ap.add_argument("--split", action="store_true",
-                    help="also time kda_chunk_fwd_split against kda_chunk_fwd on single sequences with few heads")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip timing kda_chunk_fwd_split against kda_chunk_fwd on single sequences")
     ap.add_argument("--decode-tokens", type=int, default=4,
                     help="tokens per kda_decode_multi call on the decode workload (1 skips that measurement)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -499,7 +589,7 @@ def main():
     others = []
     if not args.no_configs:
         measured = measure_peaks()
-        log(f"peaks: copy {measured['hbm_copy_gbs']:.0f} GB/s, bf16 MFMA {measured['mfma_bf16_tflops']:.0f} "
+        log(f"peaks: HBM {measured['hbm_gbs']:.0f} GB/s, bf16 MFMA {measured['mfma_bf16_tflops']:.0f} "
             f"TFLOP/s, fp32 MFMA {measured['mfma_f32_tflops']:.1f} TFLOP/s")
         for idx, warm, n in OTHER_CONFIGS:
             if idx == args.workload or (idx == 3 and args.no_long):
@@ -549,7 +639,7 @@ def main():
         dec = bench_decode()
         log(f"decode: {dec['avg_step_ms']:.4f} ms per step")
         dach = dec["step_bytes"] / (dec["avg_step_ms"] / 1e3)
-        hbm_meas = measured["hbm_copy_gbs"] if measured else None
+        hbm_meas = measured["hbm_gbs"] if measured else None
         result["decode"] = {
             "workload": dec["workload"].name, "value": dec["seq_steps_per_s"], "unit": "seq-steps/s",
             "steps": dec["steps"], "reps": dec["reps"], "ms_per_step": dec["avg_step_ms"],
@@ -576,8 +666,17 @@ def main():
                         "frac": mf / FP32_VALU_PEAK, "algorithmic_flops_per_launch": mul["call_flops"]},
                 "kernel": "decode_multi_kernel",
             }
-    if args.split:
+    if args.workload == 1 and not args.no_configs:
+        result["gate_modes"] = bench_gate_modes(pre["workload"])
+        log("gate modes: " + ", ".join(f"{k} {v['ms_per_launch']:.3f} ms" for k, v in result["gate_modes"].items()))
+        from synth.workloads import WORKLOADS
+
+        result["fused_norm"] = [bench_fused_norm(pre["workload"]), bench_fused_norm(WORKLOADS[2])]
+        log("fused norm: " + ", ".join(f"{f['workload']} {f['ms_fused']:.3f} ms against {f['ms_prefill_then_norm']:.3f}"
+                                       f" ms in two passes" for f in result["fused_norm"]))
+    if not args.no_split:
         result["split"] = bench_split()
+        log("split: " + ", ".join(f"H{c['H']} {c['speedup']:.2f}x" for c in result["split"]))
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cpu_threads(), others=not args.no_configs)
         log("oracle timed")

@@ -114,20 +114,23 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
 
 /*
  * kda_chunk_fwd followed by the output side of eq. (6) of the page "Kimi
- * K3：从三条信息流到完整系统" without its projections, fused into the
- * prefill's output store for bf16 I/O: instead of o the call writes
+ * K3：从三条信息流到完整系统" without its projections: instead of o the call
+ * writes
  *
  *   y = sigmoid(z) * o / sqrt(mean(o^2) + eps)     per (token, head) row of Dv channels,
  *
  * the head-wise RMSNorm (no learned scale) of the recurrent output, gated by
- * z = W_g x from the caller.  o itself is never written to memory.
+ * z = W_g x from the caller.
  *
  *   z   [B, T, H, Dv]  dtype  (read)
  *   y   [B, T, H, Dv]  dtype  (written)
  *
- * The norm is taken of o rounded to dtype, as kda_output_gate_norm would
- * read it.  With fp32 I/O the norm runs as a second pass over y.  Every
- * other argument is as in kda_chunk_fwd; eps must be finite and >= 0.
+ * With bf16 I/O and more (sequence, head) pairs than run as workgroup pairs
+ * at once, the norm is fused into the prefill's output store and o never
+ * reaches memory; otherwise (and with fp32 I/O) o is written into y and the
+ * norm runs in place over it, which is faster there.  Either way the norm is
+ * taken of o rounded to dtype.  Every other argument is as in kda_chunk_fwd;
+ * eps must be finite and >= 0.
  */
 kda_status kda_chunk_fwd_norm(const void* q, const void* k, const void* v, const void* a, const float* beta,
                               const float* initial_state, const void* z, float eps, void* y, float* final_state, int B,

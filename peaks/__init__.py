@@ -23,6 +23,8 @@ def _load():
         L.peaks_copy.restype = ctypes.c_int
         L.peaks_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.peaks_mfma.restype = ctypes.c_int
+        L.peaks_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+        L.peaks_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -45,7 +47,28 @@ def _best_ms(fn, reps):
     return best
 
 
-def hbm_copy(nbytes=2 << 30, reps=5):
+def hbm_read(nbytes=2 << 30, reps=5, blocks_per_cu=8):
+    """Bytes/s of one read pass over nbytes."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(blocks_per_cu * cus * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def one():
+        rc = _load().peaks_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()), nbytes,
+                                blocks_per_cu * cus, stream)
+        if rc != 0:
+            raise RuntimeError(f"peaks_read failed with hipError {rc}")
+
+    ms = _best_ms(one, reps)
+    del src, out
+    torch.cuda.empty_cache()
+    return nbytes / (ms / 1e3)
+
+
+def hbm_copy(nbytes=2 << 30, reps=5, blocks_per_cu=8):
     """Bytes/s of a device copy of nbytes (read once, written once)."""
     import torch
 
@@ -55,8 +78,8 @@ def hbm_copy(nbytes=2 << 30, reps=5):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def one():
-        rc = _load().peaks_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, 8 * cus,
-                                stream)
+        rc = _load().peaks_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                                blocks_per_cu * cus, stream)
         if rc != 0:
             raise RuntimeError(f"peaks_copy failed with hipError {rc}")
 
@@ -69,9 +92,10 @@ def hbm_copy(nbytes=2 << 30, reps=5):
     return 2 * nbytes / (ms / 1e3)
 
 
-def mfma(bf16=True, iters=4096, reps=3):
+def mfma(bf16=True, iters=4096, reps=3, shape32=False, k16=False):
     """flop/s of a loop of independent MFMAs on every SIMD (4 waves per
-    compute unit and SIMD)."""
+    compute unit and SIMD); shape32: the 32x32x16 bf16 instruction; k16: the
+    16x16x16 bf16 one."""
     import torch
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -80,7 +104,8 @@ def mfma(bf16=True, iters=4096, reps=3):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def one():
-        rc = _load().peaks_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, int(bool(bf16)), stream)
+        mode = 2 if shape32 else 3 if k16 else int(bool(bf16))
+        rc = _load().peaks_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, mode, stream)
         if rc != 0:
             raise RuntimeError(f"peaks_mfma failed with hipError {rc}")
 
