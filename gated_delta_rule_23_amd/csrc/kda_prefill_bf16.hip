@@ -28,9 +28,10 @@
  *                a lane, whole 256-byte rows), loader wave w (the chain waves
  *                with kCT = 1, the gate waves with kCT = 2) taking tensor
  *                w % 4 of q, k, a, v;
- *   gate waves:  gate(i): lane (channel, tokens 4(l/16) .. +3): g, the
- *                cumulative sums and the four scaled operands, stored
- *                channel-major;
+ *   gate waves:  gate(i): lane (channel 32g + l%32, tokens 8(l/32) .. +7)
+ *                with the per-channel gate (the scalar and no-gate modes:
+ *                two channels, tokens 4(l/16) .. +3): g, the cumulative sums
+ *                and the four scaled operands, stored channel-major;
  *   chain waves: store_o(i-5) (chain wave 0 alone with kCT = 1); prep(i-3):
  *                their tiles of W = M Kh and U = M V;
  *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
@@ -64,6 +65,12 @@ constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 16
 constexpr int kThreads = 64 * 2 * kChainWaves;  // plus one gate wave per SIMD
 constexpr int kORow = 136;     // O staging row: 128 columns + 8 pad (the four rows one 2-byte write covers hit distinct banks)
 constexpr float kGateLog2 = kGateFloor * kLog2e;
+constexpr float kInvGateLog2 = 1.0f / kGateLog2;
+
+/* g log2(e) = kGateLog2 sigmoid(a) = 1 / ((1 + 2^(-a log2 e)) / kGateLog2): the gate's log-decay in log2 units. */
+__device__ __forceinline__ float gate_log2(float a) {
+  return __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-a * kLog2e), kInvGateLog2, kInvGateLog2));
+}
 
 
 /* LDS rings.  A chunk x lives in slot x % (ring size); the ring a buffer
@@ -94,8 +101,9 @@ struct Smem {
 /* Inputs, written by the loads themselves (buffer_load ... lds: lane l's
  * bytes land at the instruction's LDS base + 16 l, or + 4 l for beta).  A
  * token-major row of 128 channels is therefore 256 bytes with no padding; its
- * 16-byte slots sit XOR-permuted by in_swz(row) to keep the transposing reads
- * of the gate and of prep free of bank conflicts. */
+ * 16-byte slots sit XOR-permuted (in_swz_ch for q, k and a under the
+ * per-channel gate, in_swz otherwise) to keep the transposing reads of the
+ * gate and of prep free of bank conflicts. */
 struct InQKA {
   alignas(16) bf16 t[3][kChunk][kD];  // q, k, a of chunk x (slot x % 3): loaded at x-2 -> gate (x)
 };
@@ -112,21 +120,35 @@ struct InBeta {
  * (h even, h odd) fall 8 slots apart. */
 __device__ __forceinline__ int in_swz(int r) { return (2 * (r & 3)) ^ (8 * ((r >> 2) & 1)); }
 __device__ __forceinline__ int in_off(int r, int col) { return r * kD + 8 * ((col >> 3) ^ in_swz(r)) + (col & 7); }
+/* q, k and a for the per-channel gate, whose lanes hold eight tokens of one
+ * channel: a half wave's transposing read touches four rows and four slots
+ * (two 16-channel tiles), which in_swz_ch spreads over 16 distinct slots. */
+__device__ __forceinline__ int in_swz_ch(int r) { return 4 * (r & 3); }
+__device__ __forceinline__ int in_off_ch(int r, int col) { return r * kD + 8 * ((col >> 3) ^ in_swz_ch(r)) + (col & 7); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-/* 16 bytes per lane from the buffer at byte voff straight into LDS at
- * lds_base + 16 lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base, and
- * an instruction reading M0 needs one wait state after the scalar write).
+/* Loads straight into LDS (buffer_load ... lds): M0 holds the LDS base, and
+ * an instruction reading M0 needs one wait state after the scalar write.
  * Written as inline assembly so that the compiler does not order every later
- * LDS access of the wave behind it: the caller waits for these loads itself
- * (vmcnt) before the workgroup barrier that publishes the data. */
-__device__ __forceinline__ void load_b128_to_lds(rsrc_t r, uint32_t lds_base, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff),
-               "s"(r)
-               : "memory", "m0");
+ * LDS access of the wave behind them: the caller waits for these loads itself
+ * (vmcnt) before the workgroup barrier that publishes the data.
+ *
+ * Four rows of 16 bytes a lane (lane l at lds_base + 16 l + 1024 j for row
+ * j): the instruction offset 1024 j is added to both the LDS and the global
+ * address, so one M0 serves all four and the global offsets v1 .. v3 take
+ * it back. */
+__device__ __forceinline__ void load_4rows_to_lds(rsrc_t r, uint32_t lds_base, int v0, int v1, int v2, int v3) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds" ::"s"(lds_base),
+      "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(r)
+      : "memory", "m0");
 }
-/* The same with 4 bytes per lane (lane l at lds_base + 4 l). */
+/* 4 bytes per lane (lane l at lds_base + 4 l). */
 __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_base), "v"(voff),
                "s"(r)
@@ -245,16 +267,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   const char* ld_seq = reinterpret_cast<const char*>((ldw == 0 ? q : ldw == 1 ? k : ldw == 2 ? a : v) + seq_off);
   const char* beta_seq = reinterpret_cast<const char*>(beta + tok0 * H + hh);
   const int beta_off = n * H * (int)sizeof(float);
+  int voff_row[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * j + h;
+    const int sw = kGate == kGateChannel && ldw < 3 ? in_swz_ch(row) : in_swz(row);
+    voff_row[j] = row * tok_bytes + 16 * (n ^ sw) - 1024 * j;
+  }
   // full: the chunks are known to be whole, their resources need no range tests
   auto dma_rows = [&](int x, bf16* dst, auto full) {
     constexpr bool kFull = decltype(full)::value;
     const rsrc_t r = make_rsrc(ld_seq + x * rows_step, kFull ? rows_full : rows_bytes(x));
     // instruction j: rows 4j .. 4j+3, lane (n, h) row 4j + h, stored slot n
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 4 * j + h;
-      load_b128_to_lds(r, (uint32_t)(uintptr_t)(lds_void*)(dst + 4 * j * kD), row * tok_bytes + 16 * (n ^ in_swz(row)));
-    }
+    // the instruction offset 1024 j adds to both addresses: the global one takes it back in voff
+    load_4rows_to_lds(r, (uint32_t)(uintptr_t)(lds_void*)dst, voff_row[0], voff_row[1], voff_row[2], voff_row[3]);
   };
   // beta (loader 0, lanes 0..15: token l) and q, k or a (loaders 0..2) of chunk i+2
   // (the scalar gate's fp32 logits, [.., H] like beta, come with beta from
@@ -618,7 +644,25 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     struct GateIn {
       bf16x4 q[2], k[2], a[2];
     };
+    // Per-channel gate: lane (l%16, h) holds channel 32g + 16(h%2) + l%16, tokens
+    // 8(h/2) .. 8(h/2)+7 (in[0]: the first four, in[1]: the next four).
+    const int gt = h >> 1, gcol = 32 * g + 16 * (h & 1);
     auto gate_read = [&](int x, GateIn& in) {
+      if constexpr (kGate == kGateChannel) {
+        // the slot's byte offset, uniform and opaque to loop strength reduction,
+        // so each read address is one add and the tensor offsets immediates
+        int slot = (x % 3) * (int)sizeof(InQKA);
+        asm volatile("" : "+s"(slot));
+        const char* tile = reinterpret_cast<const char*>(&s_qka[0].t[0][0][0]) + slot;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const char* p = tile + 2 * in_off_ch(8 * gt + 4 * r + (n >> 2), gcol + 4 * (n & 3));
+          in.q[r] = lds_tr(reinterpret_cast<const bf16*>(p));
+          in.k[r] = lds_tr(reinterpret_cast<const bf16*>(p + kChunk * kD * 2));
+          in.a[r] = lds_tr(reinterpret_cast<const bf16*>(p + 2 * kChunk * kD * 2));
+        }
+        return;
+      }
       // Lane (l%16, h) addresses row 4h + (l%16)/4, elements 32g + 16cs + 4(l%4) ..;
       // the transposing read returns channel 32g + 16cs + l%16, tokens 4h .. 4h+3.
       const bf16* tile = &s_qka[x % 3].t[0][0][0];
@@ -632,6 +676,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     };
     // 0/1 weights of the two exchanged partial sums in this lane's exclusive prefix
     const float w_odd = (h & 1) ? 1.0f : 0.0f, w_hi = h >= 2 ? 1.0f : 0.0f;
+    const float w_half = gt ? 1.0f : 0.0f;  // the per-channel gate's prefix weight
     auto gate = [&](int x, const GateIn& in, auto ragged) {
       if constexpr (kGate == kGateNone) {
         // alpha = 1: Gamma = Gamma_C = 1, so Kh = Kt = Kb = K and Qh = Q (the
@@ -653,21 +698,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         float b[4], run = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float sg = sigmoid_fast(la[j]);
+          float sg = gate_log2(la[j]);
           if constexpr (decltype(ragged)::value) sg = x * kChunk + 4 * h + j < T ? sg : 0.0f;  // padded tokens: g = 0
-          run += sg;
+          run = j == 0 ? sg : run + sg;
           b[j] = run;
         }
         const auto eo = __builtin_amdgcn_permlane16_swap(__float_as_uint(run), __float_as_uint(run), false, false);
         const float e = __uint_as_float(eo[0]), pair = e + __uint_as_float(eo[1]);
         const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
         const float z_lo = __uint_as_float(zz[0]);
-        const float prefix = kGateLog2 * fmaf(w_hi, z_lo, w_odd * e);
-        const float gam_c = __builtin_amdgcn_exp2f(kGateLog2 * (z_lo + __uint_as_float(zz[1])));
+        const float prefix = fmaf(w_hi, z_lo, w_odd * e);
+        const float gam_c = __builtin_amdgcn_exp2f(z_lo + __uint_as_float(zz[1]));
         f32x4 gam, inv;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float b2 = fmaf(kGateLog2, b[j], prefix);
+          const float b2 = b[j] + prefix;
           gam[j] = __builtin_amdgcn_exp2f(b2);
           inv[j] = __builtin_amdgcn_exp2f(-b2);
         }
@@ -684,37 +729,33 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         }
         return;
       }
-      // Sums are kept in units of sigmoid(a); g log2(e) = kGateLog2 sigmoid(a).
-      float b[2][4], run[2];
+      // Sums are kept in log2 units: c = g log2(e) summed over the lane's
+      // eight tokens, then the other half's total from the lanes 32 away.
+      float c[8];
 #pragma unroll
-      for (int cs = 0; cs < 2; ++cs) {
-        const f32x4 aa = bf16x4_to_f32(in.a[cs]);
-        run[cs] = 0.0f;
+      for (int r = 0; r < 2; ++r) {
+        const f32x4 aa = bf16x4_to_f32(in.a[r]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float sg = sigmoid_fast(aa[j]);
-          if constexpr (decltype(ragged)::value) sg = x * kChunk + 4 * h + j < T ? sg : 0.0f;  // padded tokens: g = 0
-          run[cs] += sg;
-          b[cs][j] = run[cs];
+          float sg = gate_log2(aa[j]);
+          if constexpr (decltype(ragged)::value)
+            sg = x * kChunk + 8 * gt + 4 * r + j < T ? sg : 0.0f;  // padded tokens: g = 0
+          c[4 * r + j] = r == 0 && j == 0 ? sg : c[4 * r + j - 1] + sg;
         }
       }
+      // z[0] = tokens 0..7's total, z[1] = tokens 8..15's, in every lane
+      const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[7]), __float_as_uint(c[7]), false, false);
+      const float z0 = __uint_as_float(zz[0]);
+      const float prefix = w_half * z0;
+      const float gam_c = __builtin_amdgcn_exp2f(z0 + __uint_as_float(zz[1]));
+      const int row = gcol + n;  // channel-major row of this lane's channel
 #pragma unroll
-      for (int cs = 0; cs < 2; ++cs) {
-        // Prefix over the four token groups (16-lane rows) of each channel, by
-        // row swaps in registers: e = r of rows (0, 0, 2, 2), o = of rows
-        // (1, 1, 3, 3); their sums s, swapped across the halves, give z = s of
-        // rows 0-1 and the other half's.
-        const auto eo = __builtin_amdgcn_permlane16_swap(__float_as_uint(run[cs]), __float_as_uint(run[cs]), false, false);
-        const float e = __uint_as_float(eo[0]), pair = e + __uint_as_float(eo[1]);
-        const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
-        const float z_lo = __uint_as_float(zz[0]);  // r0 + r1 in every row
-        const float prefix = kGateLog2 * fmaf(w_hi, z_lo, w_odd * e);
-        const float gam_c = __builtin_amdgcn_exp2f(kGateLog2 * (z_lo + __uint_as_float(zz[1])));
-        const f32x4 kk = bf16x4_to_f32(in.k[cs]), qq = bf16x4_to_f32(in.q[cs]);
+      for (int r = 0; r < 2; ++r) {
+        const f32x4 kk = bf16x4_to_f32(in.k[r]), qq = bf16x4_to_f32(in.q[r]);
         f32x4 kh, qh, kt, kb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float b2 = fmaf(kGateLog2, b[cs][j], prefix);
+          const float b2 = c[4 * r + j] + prefix;
           const float gam = __builtin_amdgcn_exp2f(b2);
           const float inv = __builtin_amdgcn_exp2f(-b2);
           kh[j] = kk[j] * gam;
@@ -722,13 +763,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           kt[j] = kk[j] * inv;
           kb[j] = kt[j] * gam_c;
         }
-        const int cm = (32 * g + 16 * cs) * kChunk + pl_sw;  // channel ch, tokens 4h ..
+        const int cm = row * kChunk + 4 * ((2 * gt + r) ^ (n >> 2));  // tokens 8gt + 4r .., group-permuted
         lds_put(&sm.r4[x & 3].kh[0][0] + cm, kh);
         if constexpr (!kStateOnly) lds_put(&sm.r5[x % 5].qh[0][0] + cm, qh);
         lds_put(&sm.r2[x & 1].kt[0][0] + cm, kt);
         lds_put(&sm.r5[x % 5].kb[0][0] + cm, kb);
-        if (h == 0) sm.r5[x % 5].gamma_c[n >> 2][n & 3][2 * g + cs] = gam_c;
       }
+      if (gt == 0) sm.r5[x % 5].gamma_c[n >> 2][n & 3][2 * g + (h & 1)] = gam_c;
     };
 
     // With the loads here, as on the chain waves with two workgroups per
