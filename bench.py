@@ -219,10 +219,12 @@ def measure_peaks():
     return {"hbm_copy_gbs": copy, "hbm_read_gbs": read, "hbm_gbs": max(copy, read),
             "mfma_bf16_tflops": max(bf16.values()), "mfma_bf16_tflops_by_shape": bf16,
             "mfma_f32_tflops": peaks.mfma(bf16=False) / 1e12,
+            "valu_ns_per_wave_instruction": peaks.valu_ns_per_instruction(),
             "spec": {"hbm_gbs": HBM_PEAK / 1e9, "mfma_bf16_tflops": BF16_MFMA_PEAK / 1e12,
                      "mfma_f32_tflops": FP32_MFMA_PEAK / 1e12},
             "how": "best of 5 launches: 2 GiB copy (read + written bytes) and read; MFMA loops of 8 or 16 "
-                   "independent accumulators per wave, 4 waves per SIMD"}
+                   "independent accumulators per wave, 4 waves per SIMD; VALU loops of 8 independent chains a lane "
+                   "(the time per wave64 instruction per SIMD)"}
 
 
 def bench_gate_norm(w, reps=50):
@@ -590,7 +592,8 @@ def main():
     if not args.no_configs:
         measured = measure_peaks()
         log(f"peaks: HBM {measured['hbm_gbs']:.0f} GB/s, bf16 MFMA {measured['mfma_bf16_tflops']:.0f} "
-            f"TFLOP/s, fp32 MFMA {measured['mfma_f32_tflops']:.1f} TFLOP/s")
+            f"TFLOP/s, fp32 MFMA {measured['mfma_f32_tflops']:.1f} TFLOP/s; VALU ns per wave instruction "
+            + ", ".join(f"{k} {v:.2f}" for k, v in measured["valu_ns_per_wave_instruction"].items()))
         for idx, warm, n in OTHER_CONFIGS:
             if idx == args.workload or (idx == 3 and args.no_long):
                 continue

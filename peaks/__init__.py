@@ -25,6 +25,8 @@ def _load():
         L.peaks_mfma.restype = ctypes.c_int
         L.peaks_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         L.peaks_read.restype = ctypes.c_int
+        L.peaks_valu.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.peaks_valu.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -112,3 +114,26 @@ def mfma(bf16=True, iters=4096, reps=3, shape32=False, k16=False):
     ms = _best_ms(one, reps)
     flops = blocks * 4 * iters * 8 * MFMA_FLOPS[bool(bf16)]
     return flops / (ms / 1e3)
+
+
+def valu_ns_per_instruction(iters=4096, reps=3):
+    """Nanoseconds a SIMD takes per wave64 instruction in loops of independent
+    v_exp_f32, v_rcp_f32 and v_mul_f32 (4 waves per SIMD), keyed by name."""
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    blocks = 4 * cus
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for op, name in enumerate(("v_exp_f32", "v_rcp_f32", "v_mul_f32")):
+        def one():
+            rc = _load().peaks_valu(ctypes.c_void_p(out.data_ptr()), blocks, iters, op, stream)
+            if rc != 0:
+                raise RuntimeError(f"peaks_valu failed with hipError {rc}")
+
+        ms = _best_ms(one, reps)
+        per_simd = (blocks * 4) / (cus * 4) * iters * 8  # instructions each SIMD issues
+        res[name] = ms * 1e6 / per_simd
+    return res

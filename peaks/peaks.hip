@@ -13,6 +13,9 @@
  *                     v_mfma_f32_16x16x32_bf16 (16 x 16 x 32 x 2 flops each)
  *   peaks_mfma_f32    the same with v_mfma_f32_16x16x4_f32 (16 x 16 x 4 x 2)
  *                     (and 4 independent v_mfma_f32_32x32x16_bf16 per iteration)
+ *   peaks_valu        8 independent chains a lane of v_exp_f32, v_rcp_f32 or
+ *                     v_mul_f32: how long a transcendental instruction holds
+ *                     the VALU against a plain one
  * The MFMA results are summed and stored, so nothing is optimised away.
  */
 #include <hip/hip_runtime.h>
@@ -138,6 +141,31 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ out,
   out[(size_t)blockIdx.x * kThreads + t] = s[0] + s[1] + s[2] + s[3];
 }
 
+/* op 0: v_exp_f32, 1: v_rcp_f32, 2: v_mul_f32; iters x 8 instructions a wave. */
+template <int kOp>
+__global__ __launch_bounds__(kThreads) void valu_kernel(float* __restrict__ out, int iters) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.5f + 0.001f * (float)(threadIdx.x + j);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (kOp == 0)
+        x[j] = __builtin_amdgcn_exp2f(x[j]);
+      else if constexpr (kOp == 1)
+        x[j] = __builtin_amdgcn_rcpf(x[j]);
+      else
+        x[j] = x[j] * 1.0001f;
+    }
+    // each chain stays a chain of single instructions (no reassociation)
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +204,20 @@ int peaks_mfma(float* out, int blocks, int iters, int bf16, void* stream) {
     hipLaunchKernelGGL(mfma_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
   else
     hipLaunchKernelGGL(mfma_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+/* `blocks` workgroups of 256 threads, each wave issuing iters x 8 VALU
+ * instructions of kind op (0 v_exp_f32, 1 v_rcp_f32, 2 v_mul_f32); out
+ * holds blocks x 256 floats.  Returns a hipError_t. */
+int peaks_valu(float* out, int blocks, int iters, int op, void* stream) {
+  if (blocks <= 0 || iters <= 0 || op < 0 || op > 2) return (int)hipErrorInvalidValue;
+  if (op == 0)
+    hipLaunchKernelGGL(valu_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
+  else if (op == 1)
+    hipLaunchKernelGGL(valu_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
+  else
+    hipLaunchKernelGGL(valu_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
   return (int)hipGetLastError();
 }
 
