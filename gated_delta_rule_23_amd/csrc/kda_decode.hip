@@ -158,7 +158,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __rest
 // tokens, which the workgroup stages in LDS eight tokens at a time behind one
 // barrier (thread t: channel t / 2, tokens 4 (t % 2) .. +3 of the group), and
 // it loads the next group's inputs (or the next state's first group and the
-// state itself) into registers right after staging.
+// state itself) into registers right after staging.  The gate's transcendentals
+// are single instructions (v_exp_f32, v_rcp_f32) with the log-decay summed in
+// log2 units, and the staging's q . k partial sums stay in registers (DPP and
+// lane swaps).  A state moves from its prefetch registers into the working
+// ones only after its first group is staged: the copy waits for every memory
+// access issued before it, the previous state's committing stores included,
+// and the staging gives those time to drain.
 //
 // Within a group the registers hold T = Diag(1/D_j) S_j, where D_j is the
 // product of the decays alpha of the group's tokens up to j (per key channel;
@@ -169,6 +175,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const IO* __rest
 // S = Diag(D_j) T is formed only where it is needed: at the group's end
 // before the next group, and for the committed state.
 constexpr int kMultiThreads = 256;
+constexpr float kInvGateLog2 = 1.0f / (kGateFloor * kLog2e);
 constexpr int kMultiRows = kD / 8;  // rows per lane
 constexpr int kGroupTokens = 8;     // tokens staged per LDS set
 constexpr int kStagePerThread = kGroupTokens * kD / kMultiThreads;  // 4
@@ -183,11 +190,17 @@ __device__ __forceinline__ float sum_row_pairs(float x) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
-// The sum over the 32 lanes of a wave with the same lane parity.
+// The sum over the 32 lanes of a wave with the same lane parity: rotations
+// by 8, 4 and 2 within each 16-lane row keep the parity, then the rows are
+// combined by two swaps, all in registers.
 __device__ __forceinline__ float sum_same_parity(float x) {
-#pragma unroll
-  for (int off = 2; off <= 32; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // Four consecutive output values through a buffer resource: one 8-byte
@@ -274,7 +287,7 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
   Staged in = {};
   int nc = 0, nc_next = 0;
   if (unit < units) {
-    load_state(unit, s);
+    load_state(unit, sn);
     load_group(unit, 0, in);
     nc = commit_count(unit);
   }
@@ -292,7 +305,8 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
       for (int i = 0; i < kStagePerThread; ++i) {
         if constexpr (kGate != kGateNone) {
           const float ai = kGate == kGateChannel ? Raw<IO>::f32(in.a[i]) : __uint_as_float(in.a[i]);
-          run += kGateFloor * kLog2e / (1.0f + expf(-ai));
+          // g log2(e) = -5 log2(e) sigmoid(a) = 1 / ((1 + 2^(-a log2 e)) / (-5 log2 e))
+          run += __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(-ai * kLog2e), kInvGateLog2, kInvGateLog2));
         }
         lg[i] = run;
       }
@@ -303,13 +317,20 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
         const int jj = kStagePerThread * sh + i;
         const float qi = Raw<IO>::f32(in.q[i]), ki = Raw<IO>::f32(in.k[i]);
         const float l2d = lg[i] + carry;
-        const float dd = exp2f(l2d), di = exp2f(-l2d);
+        const float dd = __builtin_amdgcn_exp2f(l2d), di = __builtin_amdgcn_exp2f(-l2d);
         s_kq[set][jj][sc] = f32x2{dd * ki, dd * qi};
         s_kd[set][jj][sc] = f32x2{ki * di, dd};
         s_v[set][jj][sc] = Raw<IO>::f32(in.v[i]);
         if (sc == 0) s_beta[set][jj] = in.b[i];
         const float part = sum_same_parity(qi * ki);
         if (lane < 2) s_qk[set][jj][w] = part;
+      }
+      // The state enters its registers after its first group is staged, so
+      // the previous state's committing stores, which the copy waits for
+      // with everything issued before it, have the staging's time to drain.
+      if (g == 0) {
+#pragma unroll
+        for (int m = 0; m < kMultiRows; ++m) s[m] = sn[m];
       }
       // inputs of the next group, or of the next state's first group with the state itself
       if (g + 1 < ngroups) {
@@ -364,8 +385,6 @@ __global__ __launch_bounds__(kMultiThreads, 2) void decode_multi_kernel(
         for (int m = 0; m < kMultiRows; ++m) s[m] *= s_kd[set][kGroupTokens - 1][r0 + 8 * m][1];
       }
     }
-#pragma unroll
-    for (int m = 0; m < kMultiRows; ++m) s[m] = sn[m];
     nc = nc_next;
     unit = next;
   }
