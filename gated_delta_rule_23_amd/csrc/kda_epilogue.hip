@@ -8,8 +8,11 @@
  *
  * Bound by HBM: a row reads o and z once and writes y once.  A lane takes 16
  * bytes of a row per operand (8 bf16 or 4 fp32 channels), so a wave moves
- * 1 KiB per access; the row's sum of squares is reduced over its lanes.
- * y may be o itself: every lane reads its elements before it writes them.
+ * 1 KiB per access, and covers four rows whose loads all go out first; the
+ * row's sum of squares is reduced over its lanes by DPP rotations, and the
+ * sigmoid and the reciprocal square root are single instructions
+ * (v_exp_f32, v_rcp_f32, v_rsq_f32).  y may be o itself: every lane reads
+ * its elements before it writes them.
  */
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -51,32 +54,59 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[8]) {
   return w;
 }
 
+// Rows a thread covers: the loads of all of them go out before any is used.
+constexpr int kNormUnroll = 4;
+
+// The sum over the lanes of one row: a row of bf16 channels spans one 16-lane
+// DPP row (four rotations), a row of fp32 channels two (then a row swap).
+template <typename IO>
+__device__ __forceinline__ float row_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  if constexpr (Lanes<IO>::kRowLanes == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
 template <typename IO>
 __global__ __launch_bounds__(kNormThreads) void gate_norm_kernel(const IO* o, const IO* z, IO* y, int64_t rows,
                                                                 float eps) {
   using L = Lanes<IO>;
+  static_assert(L::kRowLanes == 16 || L::kRowLanes == 32, "a row spans one or two DPP rows");
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * L::kRowsPerBlock + L::kRowsPerWave * (threadIdx.x >> 6) + lane / L::kRowLanes;
-  const bool live = row < rows;
-  const int64_t at = row * kD + L::kPerLane * (lane % L::kRowLanes);
-  float ov[L::kPerLane], zv[L::kPerLane];
-  u32x4 ow = {0, 0, 0, 0}, zw = {0, 0, 0, 0};
-  if (live) {
-    ow = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + at));
-    zw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + at));
+  // rows of block b: kNormUnroll slabs of kRowsPerBlock, thread row i of slab u
+  const int64_t row0 = (int64_t)blockIdx.x * (kNormUnroll * L::kRowsPerBlock) +
+                       L::kRowsPerWave * (threadIdx.x >> 6) + lane / L::kRowLanes;
+  const int col = L::kPerLane * (lane % L::kRowLanes);
+  u32x4 ow[kNormUnroll], zw[kNormUnroll];
+#pragma unroll
+  for (int u = 0; u < kNormUnroll; ++u) {
+    const int64_t row = row0 + (int64_t)u * L::kRowsPerBlock;
+    ow[u] = zw[u] = u32x4{0, 0, 0, 0};
+    if (row < rows) {
+      ow[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + row * kD + col));
+      zw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + row * kD + col));
+    }
   }
-  unpack(ow, ov, IO());
-  unpack(zw, zv, IO());
-  float ss = 0.0f;
 #pragma unroll
-  for (int j = 0; j < L::kPerLane; ++j) ss += ov[j] * ov[j];
+  for (int u = 0; u < kNormUnroll; ++u) {
+    const int64_t row = row0 + (int64_t)u * L::kRowsPerBlock;
+    float ov[L::kPerLane], zv[L::kPerLane];
+    unpack(ow[u], ov, IO());
+    unpack(zw[u], zv, IO());
+    float ss = 0.0f;
 #pragma unroll
-  for (int off = L::kRowLanes / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);  // within the row's lanes
-  const float inv = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-  float out[L::kPerLane];
+    for (int j = 0; j < L::kPerLane; ++j) ss = fmaf(ov[j], ov[j], ss);
+    const float inv = __builtin_amdgcn_rsqf(fmaf(row_sum<IO>(ss), 1.0f / kD, eps));
+    float out[L::kPerLane];
 #pragma unroll
-  for (int j = 0; j < L::kPerLane; ++j) out[j] = ov[j] * inv / (1.0f + expf(-zv[j]));
-  if (live) __builtin_nontemporal_store(pack(out), reinterpret_cast<u32x4*>(y + at));  // streamed through once
+    for (int j = 0; j < L::kPerLane; ++j) out[j] = ov[j] * inv * sigmoid_fast(zv[j]);
+    if (row < rows) __builtin_nontemporal_store(pack(out), reinterpret_cast<u32x4*>(y + row * kD + col));  // streamed through once
+  }
 }
 
 }  // namespace
@@ -84,7 +114,7 @@ __global__ __launch_bounds__(kNormThreads) void gate_norm_kernel(const IO* o, co
 hipError_t launch_output_gate_norm(const void* o, const void* z, void* y, int64_t rows, float eps, bool bf16_io,
                                    hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const int per_block = bf16_io ? Lanes<bf16>::kRowsPerBlock : Lanes<float>::kRowsPerBlock;
+  const int per_block = kNormUnroll * (bf16_io ? Lanes<bf16>::kRowsPerBlock : Lanes<float>::kRowsPerBlock);
   const unsigned grid = (unsigned)((rows + per_block - 1) / per_block);
   if (bf16_io) {
     hipLaunchKernelGGL(gate_norm_kernel<bf16>, dim3(grid), dim3(kNormThreads), 0, stream, (const bf16*)o,
