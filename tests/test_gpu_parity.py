@@ -532,6 +532,28 @@ def test_output_gate_norm_against_oracle(kda, dtype):
     assert e <= TOL[dtype] and torch.equal(y, o2) and not y[0, 5, 1].any()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_output_gate_norm_many_blocks(kda, dtype):
+    """3,500 rows (55 workgroups of 64 bf16 rows or 110 of 32 fp32 rows, each
+    lane covering four rows, the last workgroup ragged), in place and out of
+    place, against the oracle."""
+    import torch
+
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(77)
+    o = (torch.randn((1, 700, 5, 128), device="cuda", generator=g) * 0.3).to(dt)
+    z = (torch.randn((1, 700, 5, 128), device="cuda", generator=g) * 2.0).to(dt)
+    y = kda.kda_output_gate_norm(o, z, 1e-6)
+    o2 = o.clone()
+    kda.kda_output_gate_norm(o2, z, 1e-6, y=o2)
+    torch.cuda.synchronize()
+    ref = oracle.output_gate_norm(to_np(o), to_np(z), 1e-6)
+    e = rel_l2(to_np(y), ref)
+    worst = max(rel_l2(to_np(y)[0, :, h], ref[0, :, h]) for h in range(5))
+    print_case(f"  output gate norm, 3500 rows, {dtype}: rel_l2 {e:.3e}, worst head {worst:.3e}")
+    assert e <= TOL[dtype] and worst <= TOL[dtype] and torch.equal(y, o2)
+
+
 # --------------------------------------------------------------------------- packed variable-length sequences
 
 
