@@ -468,7 +468,8 @@ def host_description():
 
 def cpu_threads():
     """The host threads the oracle uses: every CPU this process may run on,
-    at most 16 (the share of host CPUs a one-GPU machine grants a job)."""
+    at most 16 (the host CPUs that go with one GPU of an eight-GPU, 128-core
+    node)."""
     avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(16, avail))
 
