@@ -96,10 +96,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   float* const states = args.states;
   const int state_every = args.state_every, n_states = args.n_states;
   const bool state_only = args.mode >= kModeFragment;      // no o
-  const bool transition = args.mode == kModeTransition;    // S0 = I, v = 0
-  const int gate_mode = args.gate;
+  // With kModeTransFrag, unit b H + h of the first half of the grid is a
+  // transition run and b H + h + U (U = gridDim.x / 2) the fragment run of
+  // the same segment; the final states land at the grid index.
   const int unit = blockIdx.x;  // b * H + h
-  const int bb = unit / H, hh = unit % H;
+  const int half_units = args.mode == kModeTransFrag ? (int)gridDim.x / 2 : 0;
+  const bool transition = args.mode == kModeTransition || unit < half_units;  // S0 = I, v = 0
+  const int gate_mode = args.gate;
+  const int seq_unit = unit >= half_units ? unit - half_units : unit;
+  const int bb = seq_unit / H, hh = seq_unit % H;
   // The sequence's first token and length: b T_all and T_all; for packed
   // sequences, cu_seqlens[b] .. cu_seqlens[b + 1] clamped to [0, T_all] (so
   // any contents of cu_seqlens keep every access inside the tensors); for
@@ -422,7 +427,7 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
                             bool bf16_io, hipStream_t stream, const PrefillOptions& opt_in) {
   PrefillOptions opt = opt_in;
   const int seqs = opt.seg_len > 0 ? B * opt.seg_count : B;
-  const int units = seqs * H;
+  const int units = seqs * H * (opt.mode == kModeTransFrag ? 2 : 1);
   if (units == 0) return hipSuccess;
   // the interval in chunks and the number of checkpoints (none: no checkpoint output)
   const int every_tokens = opt.states ? opt.state_every : 0;

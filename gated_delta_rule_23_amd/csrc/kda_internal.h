@@ -14,7 +14,9 @@ enum PrefillMode : int {
   kModeEmit = 1,       // also the state checkpoints
   kModePacked = 2,     // sequences delimited by cu_seqlens, or cut into segments
   kModeFragment = 3,   // segments: final states only (no o)
-  kModeTransition = 4  // segments: final states only, from S0 = I with v = 0 (the transition matrix)
+  kModeTransition = 4, // segments: final states only, from S0 = I with v = 0 (the transition matrix)
+  kModeTransFrag = 5   // both in one launch: units [0, U) the transitions, [U, 2U) the fragments of
+                       //      the same segments, the final states of both into one [2U, 128, 128] array
 };
 /* The gate (kda_gate of include/kda.h). */
 enum GateMode : int {

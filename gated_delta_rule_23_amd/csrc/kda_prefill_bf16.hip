@@ -160,7 +160,8 @@ __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int
 // sequences are delimited by cu_seqlens or cut into segments of seg_len
 // tokens (seg_count per sequence); kModeFragment writes only the final
 // states; kModeTransition also starts every sequence from the identity and
-// reads no v (the segment's transition matrix).
+// reads no v (the segment's transition matrix); kModeTransFrag runs both,
+// the transitions as units below trans_units and the fragments above.
 // kGate (kda_gate): the gate per key channel, one fp32 logit per token and
 // head, or none (alpha = 1).
 // kNorm (one workgroup per sequence only): y = sigmoid(z) * RMSNorm(O) is
@@ -176,13 +177,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
                                                                   int unit_end, float* states, int state_every,
                                                                   int n_states, const int* cu_seqlens, int seg_len,
                                                                   int seg_count, int last_only,
-                                                                  const bf16* __restrict__ z, float eps) {
+                                                                  const bf16* __restrict__ z, float eps,
+                                                                  int trans_units) {
   static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
   static_assert(!kNorm || kCT == 2, "the fused norm needs every value channel of a row in one workgroup");
   constexpr bool kEmit = kMode == kModeEmit;
   constexpr bool kVarlen = kMode >= kModePacked;
   constexpr bool kStateOnly = kMode >= kModeFragment;     // no O: neither Qh S nor A is formed
   constexpr bool kTransition = kMode == kModeTransition;  // S0 = I, v = 0
+  constexpr bool kTransFrag = kMode == kModeTransFrag;    // units below trans_units: transition runs
   __shared__ Smem sm;
   __shared__ InQKA s_qka[3];
   __shared__ InV s_v[3];
@@ -197,7 +200,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   const int unit = unit0 + (kCT == 2 ? (int)blockIdx.x : 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7));
   const int half = kCT == 2 ? 0 : (int)((blockIdx.x >> 3) & 1);
   if (unit >= unit_end) return;  // whole workgroup, before any barrier
-  const int bb = unit / H, hh = unit % H;
+  // A transition run (S0 = I, v = 0); with kTransFrag unit u < trans_units
+  // is the transition run and u + trans_units the fragment run of the same
+  // segment, whose final states land at index u.
+  const bool trans = kTransition || (kTransFrag && unit < trans_units);
+  const int seq_unit = kTransFrag && unit >= trans_units ? unit - trans_units : unit;
+  const int bb = seq_unit / H, hh = seq_unit % H;
   // The sequence's first token and length: b T_all and T_all, or, for packed
   // sequences, cu_seqlens[b] .. cu_seqlens[b + 1] clamped to [0, T_all] (so
   // any contents of cu_seqlens keep every access inside the tensors).
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   };
   // v of chunk i-1 (loader 3), into the slot prep reads last at iteration i-1
   auto load_v = [&](int i, auto full) {
-    if (!kTransition && ldw == 3) dma_rows(i - 1, &s_v[(i + 2) % 3].t[0][0], full);
+    if (!trans && ldw == 3) dma_rows(i - 1, &s_v[(i + 2) % 3].t[0][0], full);
   };
   auto load_inputs = [&](int i, auto full) {
     load_qka(i, full);
@@ -371,14 +379,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     const int col0 = kCT == 2 ? 32 * c : 64 * half + 16 * c;
     const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
     f32x4 sacc[kCT][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][col0 + 16 ct + l%16]
-    const bool has_s0 = !kTransition && initial_state != nullptr;  // one test, so the loads below issue back to back
+    const bool has_s0 = !trans && initial_state != nullptr;  // one test, so the loads below issue back to back
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)  // zeros, or the identity for a transition run
-          sacc[ct][rt][j] = kTransition && 16 * rt + 4 * h + j == col0 + 16 * ct + n ? 1.0f : 0.0f;
+          sacc[ct][rt][j] = trans && 16 * rt + 4 * h + j == col0 + 16 * ct + n ? 1.0f : 0.0f;
     if (has_s0) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct)
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
         f32x4 uc = {0, 0, 0, 0};  // v = 0 in a transition run: U = 0
-        if constexpr (!kTransition) {
+        if (!trans) {
           const Frag4<bf16> fv =  // B layout of V, columns col0 + 16ct ..
               f4(lds_tr(&s_v[x % 3].t[0][0] + in_off(4 * h + (n >> 2), col0 + 16 * ct + 4 * (n & 3))));
           mfma_k16(uc, fm, fv);
@@ -806,7 +814,7 @@ namespace {
 
 typedef void (*PrefillKernel)(const bf16*, const bf16*, const bf16*, const bf16*, const float*, const float*, bf16*,
                               float*, int, int, int, int, float*, int, int, const int*, int, int, int, const bf16*,
-                              float);
+                              float, int);
 
 /* The kernel for a layout, mode, gate and norm; the gate variants and the
  * fused norm exist for the plain mode only (the norm with one workgroup per
@@ -827,6 +835,7 @@ PrefillKernel pick_kernel(int mode, int gate, bool norm) {
     case kModePacked: return chunk_fwd_bf16_kernel<kCT, kModePacked, kGateChannel, false>;
     case kModeFragment: return chunk_fwd_bf16_kernel<kCT, kModeFragment, kGateChannel, false>;
     case kModeTransition: return chunk_fwd_bf16_kernel<kCT, kModeTransition, kGateChannel, false>;
+    case kModeTransFrag: return chunk_fwd_bf16_kernel<kCT, kModeTransFrag, kGateChannel, false>;
   }
   return nullptr;
 }
@@ -839,7 +848,8 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
   // B counts the kernel's sequences: with segments, B sequences of T tokens
   // each make B * seg_count of them
   const int seqs = opt.seg_len > 0 ? B * opt.seg_count : B;
-  const int units = seqs * H;
+  const int trans_units = opt.mode == kModeTransFrag ? seqs * H : 0;
+  const int units = seqs * H + trans_units;
   if (units == 0) return hipSuccess;
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
@@ -861,7 +871,8 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
     hipLaunchKernelGGL(pairs ? k_pairs : k_single, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
                        H, u0, u1, opt.states, opt.state_every, opt.n_states, opt.cu_seqlens, opt.seg_len,
-                       opt.seg_count, opt.last_only ? 1 : 0, norm ? (const bf16*)opt.z : nullptr, opt.eps);
+                       opt.seg_count, opt.last_only ? 1 : 0, norm ? (const bf16*)opt.z : nullptr, opt.eps,
+                       trans_units);
   };
   // Sequences that fit on the device at once as two workgroups each (one per
   // compute unit, whole groups of 8); the fused norm needs a whole row of O

@@ -7,20 +7,22 @@
  * each of B sequences into P segments of seg_len tokens (whole chunks; the
  * last one takes the rest) gives P times the independent work:
  *
- *   1. transition run: the first P - 1 segments of every sequence from the
- *      identity, v not read, no o written  -> M [B, P - 1, H, 128, 128]
- *   2. fragment run: the same segments from zero, no o written
- *                                           -> E [B, P - 1, H, 128, 128]
- *   3. composition: S_in[0] = S0, S_in[j + 1] = M_j S_in[j] + E_j
+ *   1. transition and fragment runs, one launch: the first P - 1 segments
+ *      of every sequence from the identity with v not read (the
+ *      transitions), and the same segments from zero (the fragments), no o
+ *      written                             -> M [B, P - 1, H, 128, 128],
+ *                                             E [B, P - 1, H, 128, 128]
+ *   2. composition: S_in[0] = S0, S_in[j + 1] = M_j S_in[j] + E_j
  *                                           -> S_in [B, P, H, 128, 128]
- *   4. final run: all P segments from S_in, writing o and, from each
+ *   3. final run: all P segments from S_in, writing o and, from each
  *      sequence's last segment, its final state.
  *
- * The prefill kernels run each step (segments are sequences whose rows
+ * The prefill kernels run steps 1 and 3 (segments are sequences whose rows
  * start at b T + j seg_len, found from the unit index, so no offsets array is
- * needed) and the composition kernel runs step 3.  Three runs of the state
- * path instead of one, for P times the (sequence, head) parallelism.  The
- * caller's workspace holds M, E and S_in.
+ * needed) and the composition kernel runs step 2.  Three passes of the state
+ * path instead of one, for P times the (sequence, head) parallelism; the
+ * first two share a launch, so that together they fill the device as one.
+ * The caller's workspace holds M, E (right after M) and S_in.
  */
 #include <mutex>
 
@@ -88,11 +90,8 @@ hipError_t launch_split(const void* q, const void* k, const void* v, const void*
   PrefillOptions frag;
   frag.seg_len = seg_len;
   frag.seg_count = P - 1;
-  frag.mode = kModeTransition;
+  frag.mode = kModeTransFrag;  // the transitions into M, the fragments into E = M + per_seg (P - 1)
   hipError_t e = launch_chunk_fwd(q, k, v, a, beta, nullptr, nullptr, M, B, T, H, bf16_io, stream, frag);
-  if (e != hipSuccess) return e;
-  frag.mode = kModeFragment;
-  e = launch_chunk_fwd(q, k, v, a, beta, nullptr, nullptr, E, B, T, H, bf16_io, stream, frag);
   if (e != hipSuccess) return e;
   e = launch_compose(M, E, initial_state, S_in, B, P, H, P - 1, stream);
   if (e != hipSuccess) return e;
