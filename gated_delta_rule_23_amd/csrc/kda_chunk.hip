@@ -21,16 +21,21 @@
  * keeps b in [-80, 0] over 16 tokens, so Kt = K e^{-b} <= e^80 |K| and every
  * factor is representable in fp32 and bf16: all tiles take the dense path.
  *
- * Mapping: one 512-thread workgroup (8 waves, two per SIMD) per (b, h).
- * Lane l of wave w owns state column 16w + l%16 and key channel 16w + l%16;
- * its group h = l/16 covers tokens 4h .. 4h+3 of a chunk.
+ * Mapping: one 512-thread workgroup (8 waves, two per SIMD) per (b, h), or,
+ * while two per (b, h) still fit on the device at once, two (kPairs), each
+ * owning 64 state columns.  Lane l of wave w gates key channel 16w + l%16
+ * and owns state column 16w + l%16 (one workgroup) or 64 half + 16w + l%16
+ * (two, waves 0..3 only; waves 4..7 then take the Gram products and the
+ * solve); its group h = l/16 covers tokens 4h .. 4h+3 of a chunk.
  *   - The 128 x 128 fp32 state stays in MFMA accumulators for the whole
- *     sequence: each wave keeps 128 x 16 of it in eight 16x16 tiles.
+ *     sequence: each chain wave keeps 128 x 16 of it in eight 16x16 tiles.
+ *     The chain's fp32 MFMAs bound the iteration; with two workgroups a
+ *     SIMD runs one chain wave instead of two.
  *   - Four chunks are in flight.  In iteration i:
  *       chain(i-3):  P = [Kh; Qh] S, [Vt; A Vt] = [M; A M] (V - Kh S),
  *                    O = Qh S + A Vt (stored straight from registers),
  *                    S <- Diag(Gamma_C) S + Kb^T Vt
- *                    (18 MFMAs per wave, all waves, their own columns);
+ *                    (18 MFMAs per chain wave, their own columns);
  *       solve(i-2):  one wave forms (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
  *                    for the nilpotent N = Diag(beta) L on MFMA, then M and A M;
  *       gram(i-1):   another wave (on another SIMD) forms the 16x16 Gram
@@ -84,9 +89,10 @@ struct ChunkArgs {
   const int* cu_seqlens;
   int seg_len, seg_count, last_only;
   int mode, gate;
+  int units, trans_units;  // units of the launch; kModeTransFrag: the transition runs among them
 };
 
-template <typename IO, typename OT>
+template <typename IO, typename OT, bool kPairs>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                                                              const IO* __restrict__ v, const IO* __restrict__ a,
                                                              const float* __restrict__ beta,
@@ -96,11 +102,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   float* const states = args.states;
   const int state_every = args.state_every, n_states = args.n_states;
   const bool state_only = args.mode >= kModeFragment;      // no o
-  // With kModeTransFrag, unit b H + h of the first half of the grid is a
-  // transition run and b H + h + U (U = gridDim.x / 2) the fragment run of
-  // the same segment; the final states land at the grid index.
-  const int unit = blockIdx.x;  // b * H + h
-  const int half_units = args.mode == kModeTransFrag ? (int)gridDim.x / 2 : 0;
+  // With kModeTransFrag, unit b H + h below args.trans_units is a
+  // transition run and b H + h + trans_units the fragment run of the same
+  // segment; the final states land at the unit index.  Two workgroups per
+  // unit come in groups of 16: slots 0..7 take column half 0 of units
+  // 8 grp .. 8 grp + 7 and slots 8..15 half 1 of the same units (dispatch
+  // deals workgroups to the XCDs round robin, so both halves of a unit share
+  // an XCD and its L2).
+  const int unit = kPairs ? 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7) : (int)blockIdx.x;  // b * H + h
+  const int half = kPairs ? (int)((blockIdx.x >> 3) & 1) : 0;
+  if (unit >= args.units) return;  // whole workgroup, before any barrier
+  const int half_units = args.mode == kModeTransFrag ? args.trans_units : 0;
   const bool transition = args.mode == kModeTransition || unit < half_units;  // S0 = I, v = 0
   const int gate_mode = args.gate;
   const int seq_unit = unit >= half_units ? unit - half_units : unit;
@@ -130,18 +142,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, h = lane >> 4;
-  const int col = 16 * wave + n;  // state column and key channel of this lane
+  const int gch = 16 * wave + n;  // key channel of this lane's gate
+  // the state column of this lane: chain waves only (all, or 0..3 with two workgroups)
+  const bool chain_wave = !kPairs || wave < 4;
+  const int col = kPairs ? 64 * half + 16 * (wave & 3) + n : gch;
   const int nchunks = (T + kChunk - 1) / kChunk;
 
   // This (b, h) sequence: rows of token t start at seq + t * H * 128.
   const int64_t tok_elems = (int64_t)H * kD;
   const int64_t seq_off = (tok0 * H + hh) * kD;
   const float* beta_seq = beta + tok0 * H + hh;
-  // Byte offsets of this lane's four tokens (4h .. 4h+3) inside a chunk.
-  int off_row[4], off_beta[4];
+  // Byte offsets of this lane's four tokens (4h .. 4h+3) inside a chunk:
+  // its gate channel (q, k, a), its state column (v, o) and beta.
+  int off_row[4], off_col[4], off_beta[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    off_row[j] = (int)(((4 * h + j) * tok_elems + col) * (int64_t)sizeof(IO));
+    off_row[j] = (int)(((4 * h + j) * tok_elems + gch) * (int64_t)sizeof(IO));
+    off_col[j] = (int)(((4 * h + j) * tok_elems + col) * (int64_t)sizeof(IO));
     off_beta[j] = (4 * h + j) * H * (int)sizeof(float);
   }
   // Chunk x of a row tensor / of beta as a buffer resource sized to the
@@ -171,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   for (int rt = 0; rt < 8; ++rt)  // zeros, or the identity for a transition run
 #pragma unroll
     for (int j = 0; j < 4; ++j) sacc[rt][j] = transition && 16 * rt + 4 * h + j == col ? 1.0f : 0.0f;
-  if (initial_state && !transition) {  // one test, so the loads issue back to back
+  if (initial_state && !transition && chain_wave) {  // one test, so the loads issue back to back
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   auto load_chain_inputs = [&](int x, int64_t rows_off, Regs& r) {
     const rsrc_t rv = make_rsrc(v_seq + rows_off, transition ? 0 : rows_bytes(x));  // v = 0 in a transition run
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.v[j] = Raw<IO>::load(rv, off_row[j]);
+    for (int j = 0; j < 4; ++j) r.v[j] = Raw<IO>::load(rv, off_col[j]);
   };
 
   // The 16x16 identity as a B operand.  A x I hands A back in accumulator
@@ -264,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     mfma_k16(tqh, frag4<OT>(qh), ident);
     mfma_k16(tkt, frag4<OT>(kt), ident);
     store_frag4<OT>(&st.kbf[wave][lane][0], frag4<OT>(kbar));  // already channel-major
-    if (h == 0) st.gamma_c[col] = gam_c;
+    if (h == 0) st.gamma_c[gch] = gam_c;
     if (n == 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st.beta[4 * h + j] = cur.b[j];  // zero past T
@@ -280,10 +297,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   auto step = [&](int i, const Regs& cur, Regs& nxt) {
     // ------------------------------------------------ loads for the next iteration
     load_gate_inputs(i + 1, rows_next, beta_next, nxt);
-    load_chain_inputs(i - 2, rows_next - 3 * rows_step, nxt);
+    if (chain_wave) load_chain_inputs(i - 2, rows_next - 3 * rows_step, nxt);
 
     // ------------------------------------------------ chain(i - 3): the serial part
-    if (i - 3 >= 0 && i - 3 < nchunks) {
+    if (chain_wave && i - 3 >= 0 && i - 3 < nchunks) {
       const int x = i - 3;
       const Stage<OT>& st = sm.st[x % kStages];
       // operands from LDS first, so their latency hides behind the conversions
@@ -325,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       // O rows 4h .. 4h+3 of this column; stores past T are dropped
       const rsrc_t ro = make_rsrc(o_seq + rows_next - 4 * rows_step, state_only ? 0 : rows_bytes(x));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Raw<IO>::store(ro, off_row[j], pq[j] + da[j]);
+      for (int j = 0; j < 4; ++j) Raw<IO>::store(ro, off_col[j], pq[j] + da[j]);
       // checkpoint: the state after token 16 (x + 1), when that is a multiple of the interval
       if (states && (x + 1) % state_every == 0 && (x + 1) / state_every <= n_states) {
         float* dst = states + ((size_t)unit * n_states + (x + 1) / state_every - 1) * kD * kD;
@@ -337,7 +354,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     }
 
     // ------------------------------------------------ solve(i - 2): one wave
-    if (i - 2 >= 0 && i - 2 < nchunks && wave == (i - 2) % kWaves) {
+    // (two workgroups per unit: on waves 4..7, which hold no state)
+    if (i - 2 >= 0 && i - 2 < nchunks && wave == (kPairs ? 4 + (i - 2) % 4 : (i - 2) % kWaves)) {
       Stage<OT>& st = sm.st[(i - 2) % kStages];
       const Frag4<OT> fnt = load_frag4<OT>(&st.nf[0][lane][0]);
       const Frag4<OT> fnc = load_frag4<OT>(&st.nf[1][lane][0]);
@@ -364,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     }
 
     // ------------------------------------------------ gram(i - 1): another wave, another SIMD
-    if (i - 1 >= 0 && i - 1 < nchunks && wave == (i + 3) % kWaves) {
+    if (i - 1 >= 0 && i - 1 < nchunks && wave == (kPairs ? 4 + (i + 1) % 4 : (i + 3) % kWaves)) {
       Stage<OT>& st = sm.st[(i - 1) % kStages];
       // C layouts (lane (n, h), register j <-> row r = 4h + j, column n):
       //   gkt = Kt Kh^T = (Kh Kt^T)^T,  gqt = Kt Qh^T = (Qh Kt^T)^T
@@ -411,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   }
 
   // ---------------------------------------------------------------- state out
-  if (write_final) {
+  if (write_final && chain_wave) {
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -427,7 +445,8 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
                             bool bf16_io, hipStream_t stream, const PrefillOptions& opt_in) {
   PrefillOptions opt = opt_in;
   const int seqs = opt.seg_len > 0 ? B * opt.seg_count : B;
-  const int units = seqs * H * (opt.mode == kModeTransFrag ? 2 : 1);
+  const int trans_units = opt.mode == kModeTransFrag ? seqs * H : 0;
+  const int units = seqs * H + trans_units;
   if (units == 0) return hipSuccess;
   // the interval in chunks and the number of checkpoints (none: no checkpoint output)
   const int every_tokens = opt.states ? opt.state_every : 0;
@@ -440,11 +459,21 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
     return launch_chunk_fwd_bf16(q, k, v, a, beta, initial_state, o, final_state, B, T, H, stream, opt);
   }
   const ChunkArgs args = {opt.states, opt.state_every, opt.n_states, opt.cu_seqlens, opt.seg_len, opt.seg_count,
-                          opt.last_only ? 1 : 0, opt.mode, opt.gate};
-  hipLaunchKernelGGL((chunk_fwd_kernel<float, float>), dim3(units), dim3(kThreads), 0, stream, (const float*)q,
-                     (const float*)k, (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state,
-                     T, H, args);
-  hipError_t e = hipGetLastError();
+                          opt.last_only ? 1 : 0, opt.mode, opt.gate, units, trans_units};
+  // Two workgroups per unit while they all fit on the device at once (one
+  // per compute unit, whole groups of 8 units).
+  int cus = 0;
+  hipError_t e = device_cu_count(stream, &cus);
+  if (e != hipSuccess) return e;
+  if (units <= 8 * (cus / 16))
+    hipLaunchKernelGGL((chunk_fwd_kernel<float, float, true>), dim3(16 * ((units + 7) / 8)), dim3(kThreads), 0, stream,
+                       (const float*)q, (const float*)k, (const float*)v, (const float*)a, beta, initial_state,
+                       (float*)o, final_state, T, H, args);
+  else
+    hipLaunchKernelGGL((chunk_fwd_kernel<float, float, false>), dim3(units), dim3(kThreads), 0, stream,
+                       (const float*)q, (const float*)k, (const float*)v, (const float*)a, beta, initial_state,
+                       (float*)o, final_state, T, H, args);
+  e = hipGetLastError();
   // fp32 I/O: the output gate and norm as a second pass over o
   if (e == hipSuccess && opt.z != nullptr)
     e = launch_output_gate_norm(o, opt.z, o, (int64_t)seqs * T * H, opt.eps, false, stream);

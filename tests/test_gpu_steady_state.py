@@ -62,14 +62,13 @@ def per_block_worst(x, ref, axes):
 def test_checkpoints_in_the_steady_loop(kda, dtype, layout, every):
     """Checkpoints every 64 or 512 tokens over 1,050 (pairs: 2 x 2
     sequences, 66 chunks, the last ragged) or 1,024 tokens (3 x 97 = 291
-    sequences: single workgroups, then pairs).  Each checkpoint, each
+    sequences: single workgroups, then pairs in bf16, single workgroups in
+    fp32).  Each checkpoint, each
     sequence's output and final state against the oracle; o and the final
     state equal kda_chunk_fwd's bit for bit."""
     import torch
 
     B, H, T = (2, 2, 1050) if layout == "pairs" else (3, 97, 1024)
-    if dtype == "f32" and layout == "mixed":
-        pytest.skip("the fp32 prefill has one layout; covered by the pairs shape")
     w = variant(WORKLOADS[2], index=200 + every + (layout == "mixed"), dtype=dtype)
     print_case(f"case checkpoints steady {dtype} {layout} B={B} T={T} H={H} every={every}")
     x = device_inputs(w, B=B, T=T, H=H)

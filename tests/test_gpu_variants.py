@@ -74,10 +74,8 @@ def _gate_inputs(w, B, T, H, mode):
 @pytest.mark.parametrize("shape", [(2, 3, 37), (1, 4, 700), (3, 97, 200)], ids=lambda s: "B%dH%dT%d" % s)
 def test_prefill_gate_modes(kda, dtype, mode, shape):
     """Ragged short, steady-state (44 chunks) and 291-sequence (single
-    workgroups, then pairs) prefills with either gate mode."""
+    workgroups, then pairs in bf16; single workgroups in fp32) prefills with either gate mode."""
     B, H, T = shape
-    if dtype == "f32" and H == 97:
-        pytest.skip("the fp32 prefill has one layout")
     w = variant(WORKLOADS[2], index=300 + T, dtype=dtype)
     print_case(f"case prefill gate {mode} {dtype} B={B} H={H} T={T}")
     x, h, a_dev, g = _gate_inputs(w, B, T, H, mode)
@@ -160,8 +158,6 @@ def test_fused_norm_against_oracle(kda, dtype, shape):
     import torch
 
     B, H, T = shape
-    if dtype == "f32" and H == 97:
-        pytest.skip("the fp32 prefill has one layout")
     w = variant(WORKLOADS[2], index=340 + T, dtype=dtype)
     print_case(f"case fused norm {dtype} B={B} H={H} T={T}")
     x = device_inputs(w, B=B, T=T, H=H)
@@ -191,11 +187,10 @@ def test_fused_norm_against_oracle(kda, dtype, shape):
 def test_split_through_the_abi(kda, dtype, B, H, T, P):
     """kda_chunk_fwd_split against the oracle and the unsplit prefill:
     segments of 1,024, 512 and 272 tokens (the last one ragged); 2 x 9 x 16 =
-    288 segment-heads run 256 single workgroups and then pairs."""
+    288 segment-heads run 256 single workgroups and then pairs (bf16) or
+    single workgroups only (fp32)."""
     import torch
 
-    if dtype == "f32" and B == 2:
-        pytest.skip("the fp32 prefill has one layout")
     w = variant(WORKLOADS[2], index=350 + P + H, dtype=dtype, s0_scale=0.3)
     print_case(f"case split abi {dtype} B={B} H={H} T={T} P={P}")
     x = device_inputs(w, B=B, T=T, H=H)
