@@ -21,12 +21,13 @@
  * keeps b in [-80, 0] over 16 tokens, so Kt = K e^{-b} <= e^80 |K| and every
  * factor is representable in fp32 and bf16: all tiles take the dense path.
  *
- * Mapping: one 512-thread workgroup (8 waves, two per SIMD) per (b, h), or,
- * while two per (b, h) still fit on the device at once, two (kPairs), each
- * owning 64 state columns.  Lane l of wave w gates key channel 16w + l%16
- * and owns state column 16w + l%16 (one workgroup) or 64 half + 16w + l%16
- * (two, waves 0..3 only; waves 4..7 then take the Gram products and the
- * solve); its group h = l/16 covers tokens 4h .. 4h+3 of a chunk.
+ * Mapping: kParts 512-thread workgroups (8 waves, two per SIMD) per (b, h):
+ * one, or, while more per (b, h) still fit on the device at once, two or
+ * four, each owning 128 / kParts state columns.  Lane l of wave w gates key
+ * channel 16w + l%16 and owns state column 16w + l%16 (one workgroup) or
+ * (128 / kParts) part + 16w + l%16 (waves w < 8 / kParts only; the other
+ * waves then take the Gram products and the solve); its group h = l/16
+ * covers tokens 4h .. 4h+3 of a chunk.
  *   - The 128 x 128 fp32 state stays in MFMA accumulators for the whole
  *     sequence: each chain wave keeps 128 x 16 of it in eight 16x16 tiles.
  *     The chain's fp32 MFMAs bound the iteration; with two workgroups a
@@ -92,7 +93,7 @@ struct ChunkArgs {
   int units, trans_units;  // units of the launch; kModeTransFrag: the transition runs among them
 };
 
-template <typename IO, typename OT, bool kPairs>
+template <typename IO, typename OT, int kParts>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                                                              const IO* __restrict__ v, const IO* __restrict__ a,
                                                              const float* __restrict__ beta,
@@ -104,13 +105,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   const bool state_only = args.mode >= kModeFragment;      // no o
   // With kModeTransFrag, unit b H + h below args.trans_units is a
   // transition run and b H + h + trans_units the fragment run of the same
-  // segment; the final states land at the unit index.  Two workgroups per
-  // unit come in groups of 16: slots 0..7 take column half 0 of units
-  // 8 grp .. 8 grp + 7 and slots 8..15 half 1 of the same units (dispatch
-  // deals workgroups to the XCDs round robin, so both halves of a unit share
-  // an XCD and its L2).
-  const int unit = kPairs ? 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7) : (int)blockIdx.x;  // b * H + h
-  const int half = kPairs ? (int)((blockIdx.x >> 3) & 1) : 0;
+  // segment; the final states land at the unit index.  With several
+  // workgroups per unit they come in groups of 8 kParts: slot s takes column
+  // part s / 8 of unit 8 grp + s % 8 (dispatch deals workgroups to the XCDs
+  // round robin, so all parts of a unit share an XCD and its L2).
+  static_assert(kParts == 1 || kParts == 2 || kParts == 4, "one, two or four workgroups per unit");
+  constexpr int kChainW = kWaves / kParts;  // waves holding state columns
+  const int unit = kParts > 1 ? 8 * (int)(blockIdx.x / (8 * kParts)) + (int)(blockIdx.x & 7) : (int)blockIdx.x;
+  const int part = kParts > 1 ? (int)((blockIdx.x >> 3) % kParts) : 0;
   if (unit >= args.units) return;  // whole workgroup, before any barrier
   const int half_units = args.mode == kModeTransFrag ? args.trans_units : 0;
   const bool transition = args.mode == kModeTransition || unit < half_units;  // S0 = I, v = 0
@@ -144,8 +146,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   const int n = lane & 15, h = lane >> 4;
   const int gch = 16 * wave + n;  // key channel of this lane's gate
   // the state column of this lane: chain waves only (all, or 0..3 with two workgroups)
-  const bool chain_wave = !kPairs || wave < 4;
-  const int col = kPairs ? 64 * half + 16 * (wave & 3) + n : gch;
+  const bool chain_wave = wave < kChainW;
+  const int col = (kD / kParts) * part + 16 * (wave % kChainW) + n;
   const int nchunks = (T + kChunk - 1) / kChunk;
 
   // This (b, h) sequence: rows of token t start at seq + t * H * 128.
@@ -354,8 +356,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     }
 
     // ------------------------------------------------ solve(i - 2): one wave
-    // (two workgroups per unit: on waves 4..7, which hold no state)
-    if (i - 2 >= 0 && i - 2 < nchunks && wave == (kPairs ? 4 + (i - 2) % 4 : (i - 2) % kWaves)) {
+    // (several workgroups per unit: on the waves that hold no state)
+    if (i - 2 >= 0 && i - 2 < nchunks &&
+        wave == (kParts > 1 ? kChainW + (i - 2) % (kWaves - kChainW) : (i - 2) % kWaves)) {
       Stage<OT>& st = sm.st[(i - 2) % kStages];
       const Frag4<OT> fnt = load_frag4<OT>(&st.nf[0][lane][0]);
       const Frag4<OT> fnc = load_frag4<OT>(&st.nf[1][lane][0]);
@@ -382,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     }
 
     // ------------------------------------------------ gram(i - 1): another wave, another SIMD
-    if (i - 1 >= 0 && i - 1 < nchunks && wave == (kPairs ? 4 + (i + 1) % 4 : (i + 3) % kWaves)) {
+    if (i - 1 >= 0 && i - 1 < nchunks &&
+        wave == (kParts > 1 ? kChainW + (i + 1) % (kWaves - kChainW) : (i + 3) % kWaves)) {
       Stage<OT>& st = sm.st[(i - 1) % kStages];
       // C layouts (lane (n, h), register j <-> row r = 4h + j, column n):
       //   gkt = Kt Kh^T = (Kh Kt^T)^T,  gqt = Kt Qh^T = (Qh Kt^T)^T
@@ -460,19 +464,23 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const v
   }
   const ChunkArgs args = {opt.states, opt.state_every, opt.n_states, opt.cu_seqlens, opt.seg_len, opt.seg_count,
                           opt.last_only ? 1 : 0, opt.mode, opt.gate, units, trans_units};
-  // Two workgroups per unit while they all fit on the device at once (one
-  // per compute unit, whole groups of 8 units).
+  // Two or four workgroups per unit while they all fit on the device at once
+  // (one per compute unit, whole groups of 8 units).
   int cus = 0;
   hipError_t e = device_cu_count(stream, &cus);
   if (e != hipSuccess) return e;
-  if (units <= 8 * (cus / 16))
-    hipLaunchKernelGGL((chunk_fwd_kernel<float, float, true>), dim3(16 * ((units + 7) / 8)), dim3(kThreads), 0, stream,
-                       (const float*)q, (const float*)k, (const float*)v, (const float*)a, beta, initial_state,
-                       (float*)o, final_state, T, H, args);
+  const int64_t groups = ((int64_t)units + 7) / 8;
+  const int parts = 32 * groups <= cus ? 4 : 16 * groups <= cus ? 2 : 1;
+  auto launch = [&](auto kernel, int64_t grid) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, (const float*)a, beta, initial_state, (float*)o, final_state, T, H, args);
+  };
+  if (parts == 4)
+    launch(chunk_fwd_kernel<float, float, 4>, 32 * groups);
+  else if (parts == 2)
+    launch(chunk_fwd_kernel<float, float, 2>, 16 * groups);
   else
-    hipLaunchKernelGGL((chunk_fwd_kernel<float, float, false>), dim3(units), dim3(kThreads), 0, stream,
-                       (const float*)q, (const float*)k, (const float*)v, (const float*)a, beta, initial_state,
-                       (float*)o, final_state, T, H, args);
+    launch(chunk_fwd_kernel<float, float, 1>, units);
   e = hipGetLastError();
   // fp32 I/O: the output gate and norm as a second pass over o
   if (e == hipSuccess && opt.z != nullptr)
