@@ -55,9 +55,12 @@ FP32_MFMA_PEAK = 157.3e12  # MI355X fp32 matrix, flop/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 PREFILL_KERNEL = "chunk_fwd_bf16_kernel"  # the kernel the bf16 prefill workload runs
 COPY_CALIBRATION_BYTES = 1 << 30  # one device-to-device copy of this many bytes (--calibrate-copy)
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n)
-                  for n in ("kda_chunk.hip", "kda_prefill_bf16.hip", "kda_bf16_tiles.h", "kda_common.h", "kda_decode.hip",
-                            "kda_epilogue.hip")]
+# the sources each measured kernel is built from: its counters stay valid while these do not change
+KERNEL_SOURCES = {
+    "chunk_fwd_bf16_kernel": ("kda_prefill_bf16.hip", "kda_bf16_tiles.h", "kda_common.h"),
+    "decode_kernel": ("kda_decode.hip", "kda_common.h"),
+    "decode_multi_kernel": ("kda_decode.hip", "kda_common.h"),
+}
 
 
 def strip_comments(text):
@@ -87,12 +90,12 @@ def strip_comments(text):
     return " ".join("".join(out).split())
 
 
-def kernel_source_sha():
-    """Hash of the kernel sources without their comments and formatting, so
-    that edits of comments keep the committed counter summary valid."""
+def kernel_source_sha(kernel):
+    """Hash of the sources of `kernel` without their comments and formatting,
+    so that edits of comments keep the committed counter summary valid."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, encoding="utf-8") as f:
+    for n in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc", n), encoding="utf-8") as f:
             h.update(strip_comments(f.read()).encode())
             h.update(b"\0")
     return h.hexdigest()[:16]
@@ -109,7 +112,7 @@ def measured_traffic(kernel):
         return None
     for line in lines:
         fields = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
-        if fields.get("kernel") == kernel and fields.get("kernel_source_sha") == kernel_source_sha():
+        if fields.get("kernel") == kernel and fields.get("kernel_source_sha") == kernel_source_sha(kernel):
             return float(fields["hbm_bytes_per_launch"])
     return None
 
