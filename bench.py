@@ -147,9 +147,24 @@ def timed_launches(fn, n, stream):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
+def timed_block(fn, n, stream):
+    """Run fn n times back to back between two HIP events on the stream the
+    kernel runs on (no event between launches, so the stream holds nothing
+    but the work).  Returns the average milliseconds per launch."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def bench_prefill(steps, warmup, workload=1):
     """kda_chunk_fwd over a whole prefill workload: warmup untimed launches,
-    then steps timed ones (HIP events around each on the launch stream)."""
+    then steps timed ones between two HIP events on the launch stream."""
     import torch
 
     import gated_delta_rule_23_amd as kda
@@ -173,7 +188,7 @@ def bench_prefill(steps, warmup, workload=1):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    per_launch = timed_launches(step, steps, stream)
+    avg_ms = timed_block(step, steps, stream)
     wall = time.perf_counter() - t0
     tokens = w.B * w.T
     per_token_head = BYTES_PER_TOKEN_HEAD_BF16 if w.dtype == "bf16" else BYTES_PER_TOKEN_HEAD_F32
@@ -181,10 +196,9 @@ def bench_prefill(steps, warmup, workload=1):
     launch_bytes = (w.B * w.T * w.H * per_token_head
                     + w.B * w.H * STATE_BYTES * (2 if x["s0"] is not None else 1))
     launch_flops = w.B * w.T * w.H * FLOPS_PER_TOKEN_HEAD
-    avg_ms = sum(per_launch) / len(per_launch)
     del x, o, S
     torch.cuda.empty_cache()
-    return dict(workload=w, tokens=tokens, wall=wall, per_launch_ms=per_launch, avg_ms=avg_ms,
+    return dict(workload=w, tokens=tokens, wall=wall, launches=steps, avg_ms=avg_ms,
                 launch_bytes=launch_bytes, launch_flops=launch_flops, gen_s=t_gen)
 
 
@@ -547,7 +561,7 @@ def config_entry(pre, peaks_measured):
     roof, mfma = prefill_fields(pre, peaks_measured)
     return {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dtype": w.dtype, "initial_state": w.s0_scale is not None,
             "tokens_per_s": pre["tokens"] / (pre["avg_ms"] / 1e3), "ms_per_launch": pre["avg_ms"],
-            "launches": len(pre["per_launch_ms"]), "roofline": roof, "mfma": mfma,
+            "launches": pre["launches"], "roofline": roof, "mfma": mfma,
             "input_generation_s": pre["gen_s"]}
 
 
