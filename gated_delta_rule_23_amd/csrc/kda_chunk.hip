@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, h = lane >> 4;
   const int gch = 16 * wave + n;  // key channel of this lane's gate
-  // the state column of this lane: chain waves only (all, or 0..3 with two workgroups)
+  // the state column of this lane: chain waves only (the first 8 / kParts)
   const bool chain_wave = wave < kChainW;
   const int col = (kD / kParts) * part + 16 * (wave % kChainW) + n;
   const int nchunks = (T + kChunk - 1) / kChunk;
