@@ -263,9 +263,9 @@ def bench_gate_norm(w, reps=50):
     for _ in range(5):
         one()
     torch.cuda.synchronize()
-    ms = timed_launches(one, reps, stream)
+    avg_ms = timed_block(one, reps, stream)
     rows = w.B * w.T * w.H
-    return dict(rows=rows, avg_ms=sum(ms) / len(ms), bytes=3 * rows * D * 2)
+    return dict(rows=rows, avg_ms=avg_ms, bytes=3 * rows * D * 2)
 
 
 # (H, T, segments) of single bf16 sequences: few heads (the split's use) up to the default workload's 96
@@ -408,10 +408,10 @@ def bench_decode(reps=3):
             s = steps[t]
             kda.kda_decode_step(s["q"], s["k"], s["v"], s["a"], s["beta"], state, o=outs[t], stream=stream)
 
-        ms = timed_launches(one, w.T, stream)
+        ms = timed_block(one, w.T, stream)  # the 64 steps back to back, as a decode loop issues them
         if rep > 0:  # the first repetition is the warm-up
-            totals.append(sum(ms))
-            per_step += ms
+            totals.append(ms * w.T)
+            per_step.append(ms)
     best = min(totals)
     unit_bytes = w.B * w.H * DECODE_BYTES_PER_UNIT
     avg_step_ms = sum(per_step) / len(per_step)
@@ -451,10 +451,10 @@ def bench_decode_multi(k_tokens, reps=3):
             c = calls[i]
             kda.kda_decode_multi(c["q"], c["k"], c["v"], c["a"], c["beta"], state, o=outs[i], stream=stream)
 
-        ms = timed_launches(one, len(calls), stream)
+        ms = timed_block(one, len(calls), stream)
         if rep > 0:
-            totals.append(sum(ms))
-            per_call += ms
+            totals.append(ms * len(calls))
+            per_call.append(ms)
     best = min(totals)
     avg_call_ms = sum(per_call) / len(per_call)
     call_bytes = w.B * w.H * (2 * STATE_BYTES + k_tokens * BYTES_PER_TOKEN_HEAD_BF16)
