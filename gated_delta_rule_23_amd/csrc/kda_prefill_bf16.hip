@@ -14,10 +14,12 @@
  * Mapping: 512-thread workgroups, 8 waves, two per SIMD.  The columns of S
  * (value channels) evolve independently given the per-chunk operands, so a
  * (b, h) sequence is served by one workgroup owning all 128 state columns or,
- * while two workgroups per sequence still fit on the device at once, by two
- * owning 64 each (kCT, the 16-column tiles per chain wave, is 2 or 1); the
- * two then repeat the column-independent per-chunk work, which costs nothing
- * on CUs that would be idle and halves the serial step each one runs.  Wave
+ * while more workgroups per sequence still fit on the device at once, by two
+ * owning 64 each or four owning 32 (kCT, the 16-column tiles per chain wave
+ * holding state, is 2 or 1; with four, chain waves 2 and 3 hold none and
+ * take the Gram products, the solve and the O stores); they then repeat the
+ * column-independent per-chunk work, which costs nothing on CUs that would
+ * be idle and shortens the serial step each one runs.  Wave
  * c < 4 (the chain wave of SIMD c) owns kCT 16-column tiles of the state
  * (8 kCT 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD
  * g) owns key channels 32g .. 32g+31 of the gate, so every SIMD pairs the
@@ -32,7 +34,8 @@
  *                with the per-channel gate (the scalar and no-gate modes:
  *                two channels, tokens 4(l/16) .. +3): g, the cumulative sums
  *                and the four scaled operands, stored channel-major;
- *   chain waves: store_o(i-5) (chain wave 0 alone with kCT = 1); prep(i-3):
+ *   chain waves: store_o(i-5) (chain wave 0 alone with two workgroups, 3
+ *                with four); prep(i-3):
  *                their tiles of W = M Kh and U = M V;
  *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
  *                S <- Diag(Gamma_C) S + Kb^T Vt; then, on chain waves 1, 2
@@ -166,7 +169,7 @@ __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int
 // head, or none (alpha = 1).
 // kNorm (one workgroup per sequence only): y = sigmoid(z) * RMSNorm(O) is
 // stored in place of O (eq. (6) without its projections).
-template <int kCT, int kMode, int kGate, bool kNorm>
+template <int kLay, int kMode, int kGate, bool kNorm>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
                                                                   const bf16* __restrict__ v,
@@ -179,7 +182,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
                                                                   int seg_count, int last_only,
                                                                   const bf16* __restrict__ z, float eps,
                                                                   int trans_units) {
-  static_assert(kCT == 1 || kCT == 2, "one or two workgroups per sequence");
+  // kLay: 2 one workgroup per sequence (two 16-column state tiles a chain
+  // wave), 1 two workgroups (one tile a chain wave), 4 four workgroups (one
+  // tile on chain waves 0 and 1; waves 2 and 3 hold no state).
+  static_assert(kLay == 1 || kLay == 2 || kLay == 4, "one, two or four workgroups per sequence");
+  constexpr int kCT = kLay == 2 ? 2 : 1;          // 16-column state tiles per state-holding chain wave
+  constexpr int kParts = kLay == 2 ? 1 : kLay == 1 ? 2 : 4;  // workgroups per sequence
   static_assert(!kNorm || kCT == 2, "the fused norm needs every value channel of a row in one workgroup");
   constexpr bool kEmit = kMode == kModeEmit;
   constexpr bool kVarlen = kMode >= kModePacked;
@@ -191,14 +199,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   __shared__ InV s_v[3];
   __shared__ InBeta s_beta[5];
   __shared__ InBeta s_ga[kGate == kGateScalar ? 5 : 1];  // scalar gate logits of chunk x (slot x % 5)
-  // This launch serves units (b * H + h) unit0 .. unit_end - 1.  kCT == 2:
-  // workgroup i takes unit unit0 + i.  kCT == 1: workgroups come in groups of
-  // 16, slots 0..7 taking column half 0 of units 8 grp .. 8 grp + 7 (from
-  // unit0) and slots 8..15 half 1 of the same units; dispatch deals
-  // workgroups to the XCDs round robin, so both halves of a unit share an XCD
-  // and its L2 (they load the same input rows).
-  const int unit = unit0 + (kCT == 2 ? (int)blockIdx.x : 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7));
-  const int half = kCT == 2 ? 0 : (int)((blockIdx.x >> 3) & 1);
+  // This launch serves units (b * H + h) unit0 .. unit_end - 1.  One
+  // workgroup per sequence: workgroup i takes unit unit0 + i.  Several:
+  // workgroups come in groups of 8 kParts, slot s taking column part s / 8 of
+  // unit 8 grp + s % 8 (from unit0); dispatch deals workgroups to the XCDs
+  // round robin, so all parts of a unit share an XCD and its L2 (they load
+  // the same input rows).
+  const int unit = unit0 + (kParts == 1 ? (int)blockIdx.x
+                                        : 8 * (int)(blockIdx.x / (8 * kParts)) + (int)(blockIdx.x & 7));
+  const int part = kParts == 1 ? 0 : (int)((blockIdx.x >> 3) % kParts);
   if (unit >= unit_end) return;  // whole workgroup, before any barrier
   // A transition run (S0 = I, v = 0); with kTransFrag unit u < trans_units
   // is the transition run and u + trans_units the fragment run of the same
@@ -376,7 +385,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   if (wave < kChainWaves) {
     // ================================================================ chain wave c: columns col0 .. col0 + 16 kCT - 1
     const int c = wave;
-    const int col0 = kCT == 2 ? 32 * c : 64 * half + 16 * c;
+    const int col0 = kCT == 2 ? 32 * c : (kD / kParts) * part + 16 * c;
+    // four workgroups per sequence: chain waves 2 and 3 hold no state
+    const bool holds_state = kParts < 4 || c < 2;
     const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
     f32x4 sacc[kCT][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][col0 + 16 ct + l%16]
     const bool has_s0 = !trans && initial_state != nullptr;  // one test, so the loads below issue back to back
@@ -387,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
         for (int j = 0; j < 4; ++j)  // zeros, or the identity for a transition run
           sacc[ct][rt][j] = trans && 16 * rt + 4 * h + j == col0 + 16 * ct + n ? 1.0f : 0.0f;
-    if (has_s0) {
+    if (has_s0 && holds_state) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
@@ -420,8 +431,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       }
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
-        f32x4 uc = {0, 0, 0, 0};  // v = 0 in a transition run: U = 0
-        if (!trans) {
+        f32x4 uc = {0, 0, 0, 0};  // v = 0 in a transition run: U = 0 (and none without state)
+        if (!trans && holds_state) {
           const Frag4<bf16> fv =  // B layout of V, columns col0 + 16ct ..
               f4(lds_tr(&s_v[x % 3].t[0][0] + in_off(4 * h + (n >> 2), col0 + 16 * ct + 4 * (n & 3))));
           mfma_k16(uc, fm, fv);
@@ -508,10 +519,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
           for (int j = 0; j < 4; ++j) dst[(size_t)(16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n] = sacc[ct][rt][j];
     };
     // O of chunk x from the LDS tile to o, 16 bytes a lane, every store
-    // instruction writing whole rows.  One state tile per chain wave: chain
-    // wave 0 (no Gram or solve) stores this workgroup's 128-byte half of all 16
-    // rows, lane (n, h) rows 2h + n/8 and 8 + 2h + n/8.  Two tiles: chain wave
-    // c stores rows 4c .. 4c+3.
+    // instruction writing whole rows.  Two workgroups per sequence: chain
+    // wave 0 (no Gram or solve) stores this workgroup's 128-byte half of all
+    // 16 rows, lane (n, h) rows 2h + n/8 and 8 + 2h + n/8.  Four: chain wave 3
+    // stores the 64-byte quarter.  One: chain wave c stores rows 4c .. 4c+3.
     u32x4 zbuf = {0, 0, 0, 0};  // z rows of the O tile stored next (kNorm)
     auto store_o = [&](int x, auto all) {
       const rsrc_t ro = make_rsrc(o_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
@@ -519,11 +530,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
         const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + cb);
         __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + cb, 0, 0);
       };
-      if constexpr (kCT == 1) {
+      if constexpr (kParts == 2) {
         if (c == 0) {
-          store_row(2 * h + (n >> 3), 128 * half + 16 * (n & 7));
-          store_row(8 + 2 * h + (n >> 3), 128 * half + 16 * (n & 7));
+          store_row(2 * h + (n >> 3), 128 * part + 16 * (n & 7));
+          store_row(8 + 2 * h + (n >> 3), 128 * part + 16 * (n & 7));
         }
+      } else if constexpr (kParts == 4) {
+        // chain wave 3 (no state): this workgroup's 64-byte quarter of all 16 rows, lane l row l / 4
+        if (c == 3) store_row(lane >> 2, 64 * part + 16 * (lane & 3));
       } else if constexpr (kNorm) {
         // y = sigmoid(z) o / sqrt(mean(o^2) + eps) over the row's 128 value
         // channels: lane (n, h) holds channels 8n .. 8n+7 of token 4c + h,
@@ -574,12 +588,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     // The two Gram products and the solve ride on chain waves 1, 2 and 3
     // (three different SIMDs), whose serial step leaves room before the
     // barrier; wave 0, which also loads beta, takes none.  Role: 0 Gram N,
-    // 1 Gram A, 2 solve, 3 none; kRole < 0 looks it up at run time.
+    // 1 Gram A, 2 solve, 3 none; with four workgroups per sequence the two
+    // waves without state take them: 4 both Gram products, 5 the solve.
+    // kRole < 0 looks it up at run time.
     auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], auto all, auto role)
                      __attribute__((always_inline)) {
       constexpr bool kAll = decltype(all)::value;
       constexpr int kRole = decltype(role)::value;
-      constexpr int kRoleOf[kChainWaves] = {3, 0, 1, 2};
+      constexpr int kRoleOf[kChainWaves] = {3, kParts == 4 ? 3 : 0, kParts == 4 ? 4 : 1, kParts == 4 ? 5 : 2};
       const int r = kRole >= 0 ? kRole : kRoleOf[c];
       // the stores go out before the input loads, which wait_inputs then leaves in flight
       if (!kStateOnly && (kAll || (i >= 5 && i - 5 < nchunks))) store_o(i - 5, all);
@@ -587,16 +603,24 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       if constexpr (kLoadsOnChain) load_qka(i, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
       if constexpr (kLoadsOnChain) load_v(i, all);
-      if (kAll || (i >= 4 && i - 4 < nchunks)) chain(i - 4, u_use);
+      if (holds_state && (kAll || (i >= 4 && i - 4 < nchunks))) chain(i - 4, u_use);
       if constexpr (kEmit)
-        if (i - 3 == next_emit && next_emit <= last_emit) {  // chunk i - 4 ends a checkpoint interval
+        if (holds_state && i - 3 == next_emit && next_emit <= last_emit) {  // chunk i - 4 ends a checkpoint interval
           emit_state(i - 4);
           next_emit += state_every;
         }
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 0) gram(i - 1, std::true_type(), std::false_type());
       if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1 && !kStateOnly)
         gram(i - 1, std::false_type(), std::true_type());
-      if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 2) solve(i - 2);
+      if constexpr (kParts == 4) {
+        if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 4) {
+          if constexpr (kStateOnly)
+            gram(i - 1, std::true_type(), std::false_type());
+          else
+            gram(i - 1, std::true_type(), std::true_type());
+        }
+      }
+      if ((kAll || (i >= 2 && i - 2 < nchunks)) && (r == 2 || (kParts == 4 && r == 5))) solve(i - 2);
       if constexpr (kLoadsOnChain) {
         wait_inputs();
       }
@@ -620,6 +644,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     };
     if constexpr (kCT == 2)
       steady(RunTimeRole());
+    else if (kParts == 4 && c < 2)
+      steady(std::integral_constant<int, 3>());
+    else if (kParts == 4 && c == 2)
+      steady(std::integral_constant<int, 4>());
+    else if (kParts == 4)
+      steady(std::integral_constant<int, 5>());
     else if (c == 1)
       steady(std::integral_constant<int, 0>());
     else if (c == 2)
@@ -632,7 +662,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     if (!kStateOnly && nchunks > 0 && nsteps < nchunks + 5)
       store_o(nchunks - 1, std::false_type());  // not reached inside the loop
 
-    if (write_final) {
+    if (write_final && holds_state) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
@@ -819,8 +849,9 @@ typedef void (*PrefillKernel)(const bf16*, const bf16*, const bf16*, const bf16*
 /* The kernel for a layout, mode, gate and norm; the gate variants and the
  * fused norm exist for the plain mode only (the norm with one workgroup per
  * sequence), others return NULL. */
-template <int kCT>
+template <int kLay>
 PrefillKernel pick_kernel(int mode, int gate, bool norm) {
+  constexpr int kCT = kLay;  // the layout (kLay of the kernel)
   if (norm) {
     if constexpr (kCT == 2) {
       if (mode == kModePlain && gate == kGateChannel) return chunk_fwd_bf16_kernel<2, kModePlain, kGateChannel, true>;
@@ -863,34 +894,37 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
   // norm runs in place over it.
   const bool norm_in_place = norm && opt.mode == kModePlain && units <= 8 * (cus / 16);
   if (norm_in_place) norm = false;
+  PrefillKernel k_quarters = pick_kernel<4>(opt.mode, opt.gate, norm);
   PrefillKernel k_pairs = pick_kernel<1>(opt.mode, opt.gate, norm);
   PrefillKernel k_single = pick_kernel<2>(opt.mode, opt.gate, norm);
   if (!k_single) return hipErrorInvalidValue;  // not instantiated: the API checks never ask for one
-  auto launch = [&](bool pairs, int u0, int u1) {
-    const unsigned grid = pairs ? (unsigned)(16 * (((int64_t)(u1 - u0) + 7) / 8)) : (unsigned)(u1 - u0);
-    hipLaunchKernelGGL(pairs ? k_pairs : k_single, dim3(grid), dim3(kThreads), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state, (bf16*)o, final_state, T,
-                       H, u0, u1, opt.states, opt.state_every, opt.n_states, opt.cu_seqlens, opt.seg_len,
-                       opt.seg_count, opt.last_only ? 1 : 0, norm ? (const bf16*)opt.z : nullptr, opt.eps,
-                       trans_units);
+  // parts: workgroups per sequence (1, 2 or 4), in groups of 8 sequences when more than one
+  auto launch = [&](int parts, int u0, int u1) {
+    const unsigned grid =
+        parts == 1 ? (unsigned)(u1 - u0) : (unsigned)(8 * parts * (((int64_t)(u1 - u0) + 7) / 8));
+    hipLaunchKernelGGL(parts == 4 ? k_quarters : parts == 2 ? k_pairs : k_single, dim3(grid), dim3(kThreads), 0,
+                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state,
+                       (bf16*)o, final_state, T, H, u0, u1, opt.states, opt.state_every, opt.n_states, opt.cu_seqlens,
+                       opt.seg_len, opt.seg_count, opt.last_only ? 1 : 0, norm ? (const bf16*)opt.z : nullptr,
+                       opt.eps, trans_units);
   };
-  // Sequences that fit on the device at once as two workgroups each (one per
-  // compute unit, whole groups of 8); the fused norm needs a whole row of O
-  // in one workgroup, so it always runs one workgroup per sequence.
+  // Sequences that fit on the device at once as four or two workgroups each
+  // (one per compute unit, whole groups of 8); the fused norm needs a whole
+  // row of O in one workgroup, so it always runs one workgroup per sequence.
+  const int quarter_units = k_quarters ? 8 * (cus / 32) : 0;
   const int pair_units = k_pairs ? 8 * (cus / 16) : 0;
-  if (units <= pair_units) {
-    launch(true, 0, units);
-  } else if (units <= cus) {
-    launch(false, 0, units);  // one round of one workgroup per sequence
+  auto fit = [&](int n) { return n <= quarter_units ? 4 : n <= pair_units ? 2 : 1; };
+  if (units <= cus) {
+    launch(fit(units), 0, units);  // one round
   } else {
     // Several rounds of one workgroup per sequence; a partial last round
-    // that fits as pairs runs as pairs, in a launch of its own.
+    // that fits as pairs or quarters runs so, in a launch of its own.
     const int rest = units % cus;
-    if (rest != 0 && rest <= pair_units) {
-      launch(false, 0, units - rest);
-      launch(true, units - rest, units);
+    if (rest != 0 && fit(rest) > 1) {
+      launch(1, 0, units - rest);
+      launch(fit(rest), units - rest, units);
     } else {
-      launch(false, 0, units);
+      launch(1, 0, units);
     }
   }
   hipError_t e = hipGetLastError();
