@@ -6,10 +6,12 @@ x 4 workgroups fit on the compute units, two while x 2 fit, else one per
 unit; beyond one round, the rest of the last round as two or four).  Most
 parity tests use few units, so they run the four-workgroup layout; the shapes
 here put the same modes through each layout: 40 units (four workgroups),
-100 (two), 356 (one round of single workgroups, then two each for the other
-100).  T = 200 is 13 chunks, the last one ragged, long enough for the loops
-without range tests.  Results are also compared across the layouts: each
-unit's outputs do not depend on how many workgroups serve it.
+13 (four, in a group of 8 units only partly filled), 100 (two), 356 (one
+round of single workgroups, then two each for the other 100) and 286 (then
+four each for the other 30).  T = 200 is 13 chunks, the last one ragged,
+long enough for the loops without range tests.  Results are also compared
+across the layouts: each unit's outputs do not depend on how many workgroups
+serve it.
 
 Reference: the page "Kimi K3：从三条信息流到完整系统", eq. (1) (the recurrence),
 section "hybrid prefix cache" (checkpoints) and section "FlashKDA 与 KCP",
@@ -26,8 +28,8 @@ from tests.gpu_common import TOL, WORKLOADS, device_inputs, host_inputs, print_c
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 T = 200
-# (B, H): 40 units, 100 units, 356 units
-SHAPES = {"four": (2, 20), "two": (4, 25), "one+two": (4, 89)}
+# (B, H): 40 units, 13 (a group of 8 only partly filled), 100, 356, 286 (a rest of 30)
+SHAPES = {"four": (2, 20), "four-ragged": (1, 13), "two": (4, 25), "one+two": (4, 89), "one+four": (2, 143)}
 
 
 @pytest.fixture(scope="module")
