@@ -682,10 +682,12 @@ def main():
                 "hbm": {"achieved": mb / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": mb / HBM_PEAK,
                         "frac_of_measured_peak": mb / 1e9 / hbm_meas if hbm_meas else None,
                         "algorithmic_bytes_per_launch": mul["call_bytes"]},
-                "traffic": measured_traffic("decode_multi_kernel"),
+                # past eight tokens a fully committed call runs as the chunkwise prefill, whose
+                # counters are taken on the prefill workload, not on this one
+                "traffic": measured_traffic("decode_multi_kernel") if mul["k"] <= 8 else None,
                 "alu": {"achieved": mf / 1e12, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
                         "frac": mf / FP32_VALU_PEAK, "algorithmic_flops_per_launch": mul["call_flops"]},
-                "kernel": "decode_multi_kernel",
+                "kernel": "decode_multi_kernel" if mul["k"] <= 8 else "chunk_fwd_bf16_kernel",
             }
     if args.workload == 1 and not args.no_configs:
         result["gate_modes"] = bench_gate_modes(pre["workload"])

@@ -425,6 +425,17 @@ hipError_t launch_decode_multi(const void* q, const void* k, const void* v, cons
   // One token, every state committed: the [B, 1, H, .] rows are the single
   // step's [B, H, .] rows, and its kernel streams the state faster.
   if (K == 1 && !n_commit) return launch_decode(q, k, v, a, beta, state, o, units, bf16_io, gate, stream);
+  // More than one staging group, every token committed: that is a prefill of
+  // K tokens from the state into the state (also one read and one write of
+  // it, the initial state read before the final one is written), whose
+  // chunkwise MFMA form costs nearly the same for any K up to 32 while this
+  // kernel's token loop grows with K (256 x 96 states: K = 9 0.79 against
+  // 0.83 ms, K = 16 0.82 against 1.16 ms, K = 32 0.94 against 2.08 ms).
+  if (K > kGroupTokens && !n_commit) {
+    PrefillOptions opt;
+    opt.gate = gate;
+    return launch_chunk_fwd(q, k, v, a, beta, state, o, state, units / H, K, H, bf16_io, stream, opt);
+  }
   int cus = 0;
   const hipError_t err = device_cu_count(stream, &cus);
   if (err != hipSuccess) return err;

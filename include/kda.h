@@ -286,9 +286,11 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, co
  *             device memory on the host, so it cannot reject them)
  *
  * K = 0 (or B * H = 0) enqueues nothing.  With K = 1 and n_commit NULL the
- * result is that of kda_decode_step.  K * H is at most 4194303 (a sequence's
- * K rows of one tensor must span less than 2^31 bytes); larger products fail
- * with KDA_ERR_UNSUPPORTED.
+ * result is that of kda_decode_step; with K > 8 and n_commit NULL, that of
+ * kda_chunk_fwd over the K tokens with state as both initial and final state
+ * (the chunkwise form, cheaper there than the token loop).  K * H is at
+ * most 4194303 (a sequence's K rows of one tensor must span less than 2^31
+ * bytes); larger products fail with KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_decode_multi(const void* q, const void* k, const void* v, const void* a, const float* beta,
                             float* state, void* o, const int* n_commit, int B, int K, int H, int Dk, int Dv,

@@ -735,6 +735,45 @@ def test_decode_multi_grid_stride_ragged_counts(kda, dtype):
     assert torch.equal(state[uncommitted], x["s0"][uncommitted])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("K", [9, 16, 40])
+def test_decode_multi_long_all_committed(kda, dtype, gate, K):
+    """More than eight tokens with no commit counts: the call runs as the
+    chunkwise prefill from the state into the state.  Against the oracle, bit
+    for bit against kda_chunk_fwd with the state as S0, and against the
+    multi-token kernel (the same call with every count K).  K = 40 is two
+    full chunks and a ragged one; 200 states fill several workgroup rounds."""
+    import torch
+
+    w = variant(WORKLOADS[4], index=300 + K, dtype=dtype)
+    B, H = 8, 25
+    print_case(f"case decode multi long {dtype} gate={gate} B={B} K={K} H={H}")
+    x = device_inputs(w, B=B, T=K, H=H)
+    h = host_inputs(w, nb=B, nt=K, nh=H)
+    if gate == "channel":
+        a_dev, g = x["a"], oracle.gate(synth.to_f64(h["a"]))
+    elif gate == "scalar":
+        a_dev = x["a"][..., 0].float().contiguous()
+        g = np.repeat(oracle.gate(synth.to_f64(h["a"])[..., :1]), 128, axis=3)
+    else:
+        a_dev, g = None, np.zeros((B, K, H, 128))
+    state = x["s0"].clone()
+    o = kda.kda_decode_multi_gated(x["q"], x["k"], x["v"], a_dev, x["beta"], state, gate=gate)
+    o_p, S_p = kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], a_dev, x["beta"], gate=gate, initial_state=x["s0"])
+    state_m = x["s0"].clone()
+    o_m = kda.kda_decode_multi_gated(x["q"], x["k"], x["v"], a_dev, x["beta"], state_m, gate=gate,
+                                     n_commit=torch.full((B,), K, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_p) and torch.equal(state, S_p)
+    o_ref, S_ref = oracle.forward(synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]),
+                                  h["beta"].astype(np.float64), g=g, s0=h["s0"].astype(np.float64))
+    e = [rel_l2(to_np(o), o_ref), rel_l2(to_np(state), S_ref), rel_l2(to_np(o_m), o_ref),
+         rel_l2(to_np(state_m), S_ref)]
+    print_case("  rel_l2 prefill route o/S, multi-token kernel o/S: " + " ".join(f"{v:.2e}" for v in e))
+    assert max(e) <= TOL[dtype]
+
+
 def test_decode_multi_verify_then_commit(kda):
     """The speculative flow: verify K drafted tokens without committing
     (n_commit = 0: outputs only, state untouched), then replay the accepted

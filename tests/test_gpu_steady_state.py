@@ -189,7 +189,8 @@ def test_decode_saturated_gates(kda, dtype):
 def test_decode_multi_saturated_two_groups(kda, dtype):
     """Sixteen tokens in one call (two full eight-token groups) with every
     channel at g = -5, so each group's decay product is exactly e^-40 on
-    every channel; all committed."""
+    every channel; all committed, once with the counts given (the multi-token
+    kernel) and once without (then the call runs as the chunkwise prefill)."""
     import torch
 
     B, K, H = 2, 16, 3
@@ -197,10 +198,12 @@ def test_decode_multi_saturated_two_groups(kda, dtype):
     arrays["a"][:] = 30.0
     x = _upload(dtype, arrays)
     hx = _as_device_sees(x)
-    state = x["s0"].clone()
-    o = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], state)
-    torch.cuda.synchronize()
     o_ref, S_ref = oracle.forward(hx["q"], hx["k"], hx["v"], hx["beta"], a=hx["a"], s0=hx["s0"])
-    eo, es = rel_l2(to_np(o), o_ref), rel_l2(to_np(state), S_ref)
-    print_case(f"  decode multi all-saturated {dtype}: rel_l2 o={eo:.2e} S={es:.2e}")
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    for route, nc in (("multi-token kernel", torch.full((B,), K, dtype=torch.int32, device="cuda")),
+                      ("prefill", None)):
+        state = x["s0"].clone()
+        o = kda.kda_decode_multi(x["q"], x["k"], x["v"], x["a"], x["beta"], state, n_commit=nc)
+        torch.cuda.synchronize()
+        eo, es = rel_l2(to_np(o), o_ref), rel_l2(to_np(state), S_ref)
+        print_case(f"  decode multi all-saturated {dtype}, {route}: rel_l2 o={eo:.2e} S={es:.2e}")
+        assert eo <= TOL[dtype] and es <= TOL[dtype], route
