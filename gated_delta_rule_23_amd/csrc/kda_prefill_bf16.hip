@@ -11,7 +11,8 @@
  * Folding M into W and U before the state arrives leaves three MFMA rounds
  * on the serial path (W S and Qh S, then A Vt and the state update).
  *
- * Mapping: 512-thread workgroups, 8 waves, two per SIMD.  The columns of S
+ * Mapping: 512-thread workgroups, 8 waves, two per SIMD (768 threads, three
+ * per SIMD, with two workgroups per sequence).  The columns of S
  * (value channels) evolve independently given the per-chunk operands, so a
  * (b, h) sequence is served by one workgroup owning all 128 state columns or,
  * while more workgroups per sequence still fit on the device at once, by two
@@ -23,26 +24,32 @@
  * c < 4 (the chain wave of SIMD c) owns kCT 16-column tiles of the state
  * (8 kCT 16x16 fp32 accumulator tiles) and wave 4 + g (the gate wave of SIMD
  * g) owns key channels 32g .. 32g+31 of the gate, so every SIMD pairs the
- * MFMA-heavy serial step with the VALU-heavy gate.  Iteration i of the main
- * loop does, separated by one workgroup barrier:
+ * MFMA-heavy serial step with the VALU-heavy gate.  With two workgroups per
+ * sequence, wave 8 + b (the helper wave of SIMD b) takes from the chain
+ * waves all they do besides U and the serial step: the input loads, W, the
+ * O stores, the Gram products and the solve.  Iteration i of the main loop
+ * does, separated by one workgroup barrier:
  *   inputs:      beta, q, k, a of chunk i+2 and v of chunk i-1 loaded
  *                straight into LDS token-major (buffer_load ... lds, 16 bytes
- *                a lane, whole 256-byte rows), loader wave w (the chain waves
- *                with kCT = 1, the gate waves with kCT = 2) taking tensor
- *                w % 4 of q, k, a, v;
+ *                a lane, whole 256-byte rows), loader wave w (the helper
+ *                waves with two workgroups per sequence, the chain waves with
+ *                four, the gate waves with one) taking tensor w % 4 of q, k,
+ *                a, v;
  *   gate waves:  gate(i): lane (channel 32g + l%32, tokens 8(l/32) .. +7)
  *                with the per-channel gate (the scalar and no-gate modes:
  *                two channels, tokens 4(l/16) .. +3): g, the cumulative sums
  *                and the four scaled operands, stored channel-major;
- *   chain waves: store_o(i-5) (chain wave 0 alone with two workgroups, 3
- *                with four); prep(i-3):
- *                their tiles of W = M Kh and U = M V;
+ *   chain waves: store_o(i-5) (helper wave 0 with two workgroups, chain
+ *                wave 3 with four); prep(i-3):
+ *                their tiles of W = M Kh (the helper waves' with two) and
+ *                U = M V;
  *                chain(i-4): P = [W; Qh] S, Vt = U - P_W, O = P_Q + A Vt,
  *                S <- Diag(Gamma_C) S + Kb^T Vt; then, on chain waves 1, 2
- *                and 3, gram(i-1) as two products (Kt Kh^T masked into N,
- *                Kt Qh^T into A) and solve(i-2): (I + N)^{-1} =
- *                (I - N)(I + N^2)(I + N^4)(I + N^8) (N is nilpotent, the
- *                product is exact) and M.
+ *                and 3 (helper waves 1, 2, 3 with two workgroups, chain
+ *                waves 2 and 3 with four), gram(i-1) as two products (Kt
+ *                Kh^T masked into N, Kt Qh^T into A) and solve(i-2):
+ *                (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) (N is
+ *                nilpotent, the product is exact) and M.
  * Operands change between token-major and channel-major through
  * ds_read_b64_tr_b16, which transposes 16-bit elements across the lanes of
  * each 16-lane group while it reads: lane i, element j of the result is
@@ -64,8 +71,10 @@
 namespace kda {
 namespace {
 
-constexpr int kChainWaves = 4;                // waves 0..3: the serial part, 16 kCT state columns each
-constexpr int kThreads = 64 * 2 * kChainWaves;  // plus one gate wave per SIMD
+constexpr int kChainWaves = 4;  // waves 0..3: the serial part, 16 kCT state columns each
+/* Threads of a workgroup: a chain and a gate wave per SIMD, and with two
+ * workgroups per sequence (kLay 1) a helper wave per SIMD as well. */
+constexpr int threads_of(int lay) { return 64 * (lay == 1 ? 3 : 2) * kChainWaves; }
 constexpr int kORow = 136;     // O staging row: 128 columns + 8 pad (the four rows one 2-byte write covers hit distinct banks)
 constexpr float kGateLog2 = kGateFloor * kLog2e;
 constexpr float kInvGateLog2 = 1.0f / kGateLog2;
@@ -170,7 +179,7 @@ __device__ __forceinline__ void load_b32_to_lds(rsrc_t r, uint32_t lds_base, int
 // kNorm (one workgroup per sequence only): y = sigmoid(z) * RMSNorm(O) is
 // stored in place of O (eq. (6) without its projections).
 template <int kLay, int kMode, int kGate, bool kNorm>
-__global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
+__global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const bf16* __restrict__ q,
                                                                   const bf16* __restrict__ k,
                                                                   const bf16* __restrict__ v,
                                                                   const bf16* __restrict__ a,
@@ -274,12 +283,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
   const int tr_sw = (4 * h + (n >> 2)) * kChunk + 4 * ((n & 3) ^ h);
 
   // ---------------------------------------------------------------- inputs
-  // Loader wave w (the chain waves with two workgroups per sequence, whose
-  // serial step leaves room; else the gate waves) loads tensor w % 4 (q, k,
-  // a, v) straight into LDS: in iteration i, q, k or a of chunk i+2 and v of
-  // chunk i-1 (needed only by prep, three iterations later), four
-  // instructions of four rows each; loader 0 also beta of chunk i+2.
-  constexpr bool kLoadsOnChain = kCT == 1;
+  // Loader wave w (the helper waves with two workgroups per sequence, the
+  // chain waves with four, whose serial step leaves room, the gate waves
+  // with one) loads tensor w % 4 (q, k, a, v) straight into LDS: in
+  // iteration i, q, k or a of chunk i+2 and v of chunk i-1 (needed only by
+  // prep, three iterations later), four instructions of four rows each;
+  // loader 0 also beta of chunk i+2.
+  constexpr bool kHelp = kLay == 1;  // waves 8..11: one helper wave per SIMD
+  constexpr bool kLoadsOnChain = kLay == 4;
+  constexpr bool kLoadsOnGate = kLay == 2;
   const int ldw = wave & 3;
   const char* ld_seq = reinterpret_cast<const char*>((ldw == 0 ? q : ldw == 1 ? k : ldw == 2 ? a : v) + seq_off);
   const char* beta_seq = reinterpret_cast<const char*>(beta + tok0 * H + hh);
@@ -382,13 +394,87 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     lds_put(&sm.r2[x & 1].mt[0][0] + pl_sw, m);        // M^T, rows c
   };
 
+  // ---------------------------------------------------------------- prep_w(x): W tiles
+  // W = M Kh for key channels 32b .. 32b+31 (all 128 across b = 0..3: every
+  // workgroup needs all of W), from fm, the A layout of M.
+  auto m_frag = [&](int x) { return f4(lds_tr(&sm.r2[x & 1].mt[0][0] + tr_sw)); };
+  auto prep_w = [&](int x, int b, const Frag4<bf16>& fm) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int blk = (32 * b + 16 * ct) * kChunk;  // rows 32b + 16ct ..
+      const Frag4<bf16> fkh = f4(lds_b64(&sm.r4[x & 3].kh[0][0] + blk + pl_sw));  // B layout of Kh
+      f32x4 wc = {0, 0, 0, 0};
+      mfma_k16(wc, fm, fkh);
+      lds_put(&sm.r2[x & 1].w[0][0] + blk + pl_sw, wc);  // channel-major W
+    }
+  };
+
+  // ---------------------------------------------------------------- store_o(x): O to HBM
+  // O of chunk x from the LDS tile to o, 16 bytes a lane, every store
+  // instruction writing whole rows, by wave c of the chain waves (or of the
+  // helper waves).  Two workgroups per sequence: helper wave 0 stores this
+  // workgroup's 128-byte half of all 16 rows, lane (n, h) rows 2h + n/8 and
+  // 8 + 2h + n/8.  Four: chain wave 3 stores the 64-byte quarter.  One:
+  // chain wave c stores rows 4c .. 4c+3.
+  const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
+  u32x4 zbuf = {0, 0, 0, 0};  // z rows of the O tile stored next (kNorm)
+  auto store_o = [&](int x, auto all, int c) {
+    const rsrc_t ro = make_rsrc(o_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
+    auto store_row = [&](int tok, int cb) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + cb);
+      __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + cb, 0, 0);
+    };
+    if constexpr (kParts == 2) {
+      store_row(2 * h + (n >> 3), 128 * part + 16 * (n & 7));
+      store_row(8 + 2 * h + (n >> 3), 128 * part + 16 * (n & 7));
+    } else if constexpr (kParts == 4) {
+      // chain wave 3 (no state): this workgroup's 64-byte quarter of all 16 rows, lane l row l / 4
+      store_row(lane >> 2, 64 * part + 16 * (lane & 3));
+    } else if constexpr (kNorm) {
+      // y = sigmoid(z) o / sqrt(mean(o^2) + eps) over the row's 128 value
+      // channels: lane (n, h) holds channels 8n .. 8n+7 of token 4c + h,
+      // and the 16 lanes of a DPP row hold the whole row.
+      const int tok = 4 * c + h;
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + 16 * n);
+      float f[8], ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(ov[e] << 16);
+        f[2 * e + 1] = __uint_as_float(ov[e] & 0xffff0000u);
+        ss = fmaf(f[2 * e], f[2 * e], ss);
+        ss = fmaf(f[2 * e + 1], f[2 * e + 1], ss);
+      }
+      ss += row_ror<8>(ss);
+      ss += row_ror<4>(ss);
+      ss += row_ror<2>(ss);
+      ss += row_ror<1>(ss);
+      const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / kD, eps));
+      u32x4 yv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y0 = f[2 * e] * r * sigmoid_fast(__uint_as_float(zbuf[e] << 16));
+        const float y1 = f[2 * e + 1] * r * sigmoid_fast(__uint_as_float(zbuf[e] & 0xffff0000u));
+        const bf16x2 yb = __builtin_convertvector(f32x2{y0, y1}, bf16x2);  // round to nearest even
+        yv[e] = __builtin_bit_cast(uint32_t, yb);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(yv, ro, tok * tok_bytes + 16 * n, 0, 0);
+    } else {
+      store_row(4 * c + h, 16 * n);
+    }
+  };
+  // the wave that stores O: chain wave 3 with four workgroups, helper wave 0 with two, every chain wave with one
+  auto stores_o = [&](int c) { return kParts == 4 ? c == 3 : kParts == 2 ? c == 0 : true; };
+
   if (wave < kChainWaves) {
     // ================================================================ chain wave c: columns col0 .. col0 + 16 kCT - 1
     const int c = wave;
+    // With three waves a SIMD, the serial step goes first when the chain wave
+    // and another are both ready to issue (399 against 403 us on 8K tokens x
+    // 96 heads; a higher priority for the helper waves instead: 412 us).
+    if constexpr (kHelp) __builtin_amdgcn_s_setprio(1);
     const int col0 = kCT == 2 ? 32 * c : (kD / kParts) * part + 16 * c;
     // four workgroups per sequence: chain waves 2 and 3 hold no state
     const bool holds_state = kParts < 4 || c < 2;
-    const char* o_seq = reinterpret_cast<const char*>(o + seq_off);
     f32x4 sacc[kCT][8];  // [column tile][row tile]: lane holds S[16 rt + 4h + j][col0 + 16 ct + l%16]
     const bool has_s0 = !trans && initial_state != nullptr;  // one test, so the loads below issue back to back
 #pragma unroll
@@ -417,18 +503,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     for (int ct = 0; ct < kCT; ++ct) ua[ct] = ub[ct] = f32x4{0, 0, 0, 0};
 
     // ------------------------------------------------------------ prep(x): W and U tiles
-    // W = M Kh for key channels 32c .. 32c+31 (all 128 across the four waves,
-    // every workgroup needs all of W); U = M V for this wave's state columns.
+    // W for key channels 32c .. 32c+31 (on the helper waves when there are
+    // any); U = M V for this wave's state columns.
     auto prep = [&](int x, f32x4 (&u_out)[kCT]) {
-      const Frag4<bf16> fm = f4(lds_tr(&sm.r2[x & 1].mt[0][0] + tr_sw));  // A layout of M
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int blk = (32 * c + 16 * ct) * kChunk;  // rows 32c + 16ct ..
-        const Frag4<bf16> fkh = f4(lds_b64(&sm.r4[x & 3].kh[0][0] + blk + pl_sw));  // B layout of Kh
-        f32x4 wc = {0, 0, 0, 0};
-        mfma_k16(wc, fm, fkh);
-        lds_put(&sm.r2[x & 1].w[0][0] + blk + pl_sw, wc);  // channel-major W
-      }
+      const Frag4<bf16> fm = m_frag(x);  // A layout of M
+      if constexpr (!kHelp) prep_w(x, c, fm);
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
         f32x4 uc = {0, 0, 0, 0};  // v = 0 in a transition run: U = 0 (and none without state)
@@ -518,58 +597,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
 #pragma unroll
           for (int j = 0; j < 4; ++j) dst[(size_t)(16 * rt + 4 * h + j) * kD + col0 + 16 * ct + n] = sacc[ct][rt][j];
     };
-    // O of chunk x from the LDS tile to o, 16 bytes a lane, every store
-    // instruction writing whole rows.  Two workgroups per sequence: chain
-    // wave 0 (no Gram or solve) stores this workgroup's 128-byte half of all
-    // 16 rows, lane (n, h) rows 2h + n/8 and 8 + 2h + n/8.  Four: chain wave 3
-    // stores the 64-byte quarter.  One: chain wave c stores rows 4c .. 4c+3.
-    u32x4 zbuf = {0, 0, 0, 0};  // z rows of the O tile stored next (kNorm)
-    auto store_o = [&](int x, auto all) {
-      const rsrc_t ro = make_rsrc(o_seq + x * rows_step, decltype(all)::value ? rows_full : rows_bytes(x));
-      auto store_row = [&](int tok, int cb) {
-        const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + cb);
-        __builtin_amdgcn_raw_buffer_store_b128(val, ro, tok * tok_bytes + cb, 0, 0);
-      };
-      if constexpr (kParts == 2) {
-        if (c == 0) {
-          store_row(2 * h + (n >> 3), 128 * part + 16 * (n & 7));
-          store_row(8 + 2 * h + (n >> 3), 128 * part + 16 * (n & 7));
-        }
-      } else if constexpr (kParts == 4) {
-        // chain wave 3 (no state): this workgroup's 64-byte quarter of all 16 rows, lane l row l / 4
-        if (c == 3) store_row(lane >> 2, 64 * part + 16 * (lane & 3));
-      } else if constexpr (kNorm) {
-        // y = sigmoid(z) o / sqrt(mean(o^2) + eps) over the row's 128 value
-        // channels: lane (n, h) holds channels 8n .. 8n+7 of token 4c + h,
-        // and the 16 lanes of a DPP row hold the whole row.
-        const int tok = 4 * c + h;
-        const u32x4 ov = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sm.r2[x & 1].ost[tok][0]) + 16 * n);
-        float f[8], ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[2 * e] = __uint_as_float(ov[e] << 16);
-          f[2 * e + 1] = __uint_as_float(ov[e] & 0xffff0000u);
-          ss = fmaf(f[2 * e], f[2 * e], ss);
-          ss = fmaf(f[2 * e + 1], f[2 * e + 1], ss);
-        }
-        ss += row_ror<8>(ss);
-        ss += row_ror<4>(ss);
-        ss += row_ror<2>(ss);
-        ss += row_ror<1>(ss);
-        const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / kD, eps));
-        u32x4 yv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y0 = f[2 * e] * r * sigmoid_fast(__uint_as_float(zbuf[e] << 16));
-          const float y1 = f[2 * e + 1] * r * sigmoid_fast(__uint_as_float(zbuf[e] & 0xffff0000u));
-          const bf16x2 yb = __builtin_convertvector(f32x2{y0, y1}, bf16x2);  // round to nearest even
-          yv[e] = __builtin_bit_cast(uint32_t, yb);
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(yv, ro, tok * tok_bytes + 16 * n, 0, 0);
-      } else {
-        store_row(4 * c + h, 16 * n);
-      }
-    };
     // z of chunk x for the fused norm, one iteration before its rows are stored
     const char* z_seq = reinterpret_cast<const char*>(z + seq_off);
     auto load_z = [&](int x, auto all) {
@@ -585,20 +612,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
       wait_inputs();
     }
     block_sync();  // inputs of chunk 0 in LDS
-    // The two Gram products and the solve ride on chain waves 1, 2 and 3
-    // (three different SIMDs), whose serial step leaves room before the
-    // barrier; wave 0, which also loads beta, takes none.  Role: 0 Gram N,
-    // 1 Gram A, 2 solve, 3 none; with four workgroups per sequence the two
-    // waves without state take them: 4 both Gram products, 5 the solve.
-    // kRole < 0 looks it up at run time.
+    // With one workgroup per sequence the two Gram products and the solve
+    // ride on chain waves 1, 2 and 3 (three different SIMDs), whose serial
+    // step leaves room before the barrier; wave 0 takes none.  Role: 0 Gram
+    // N, 1 Gram A, 2 solve, 3 none; with four workgroups per sequence the
+    // two waves without state take them: 4 both Gram products, 5 the solve;
+    // with two, the helper waves do, and the chain waves take none.  kRole <
+    // 0 looks it up at run time.
     auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], auto all, auto role)
                      __attribute__((always_inline)) {
       constexpr bool kAll = decltype(all)::value;
       constexpr int kRole = decltype(role)::value;
       constexpr int kRoleOf[kChainWaves] = {3, kParts == 4 ? 3 : 0, kParts == 4 ? 4 : 1, kParts == 4 ? 5 : 2};
-      const int r = kRole >= 0 ? kRole : kRoleOf[c];
+      const int r = kHelp ? 3 : kRole >= 0 ? kRole : kRoleOf[c];
       // the stores go out before the input loads, which wait_inputs then leaves in flight
-      if (!kStateOnly && (kAll || (i >= 5 && i - 5 < nchunks))) store_o(i - 5, all);
+      if (!kHelp && !kStateOnly && stores_o(c) && (kAll || (i >= 5 && i - 5 < nchunks))) store_o(i - 5, all, c);
       if (kNorm && (kAll || (i >= 4 && i - 4 < nchunks))) load_z(i - 4, all);
       if constexpr (kLoadsOnChain) load_qka(i, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
@@ -633,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     using RunTimeRole = std::integral_constant<int, -1>;
     // Iterations 5 <= i <= nchunks - 4 have every section active and load a
     // whole chunk (i + 2 < nchunks - 1): those run without range tests (pairs
-    // start at even i).  With one state tile per chain wave they run in one
+    // start at even i).  With four workgroups per sequence they run in one
     // copy of the loop per role, so that a wave's Gram or solve products share
     // a basic block with its chain step and the compiler interleaves the two
     // dependency chains; with two tiles the copies would spill registers.
@@ -644,6 +672,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     };
     if constexpr (kCT == 2)
       steady(RunTimeRole());
+    else if constexpr (kHelp)
+      steady(std::integral_constant<int, 3>());
     else if (kParts == 4 && c < 2)
       steady(std::integral_constant<int, 3>());
     else if (kParts == 4 && c == 2)
@@ -659,8 +689,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     else
       steady(std::integral_constant<int, 3>());
     for (; i < nsteps; i += 2) step2(i, std::false_type(), RunTimeRole());
-    if (!kStateOnly && nchunks > 0 && nsteps < nchunks + 5)
-      store_o(nchunks - 1, std::false_type());  // not reached inside the loop
+    if (!kHelp && !kStateOnly && stores_o(c) && nchunks > 0 && nsteps < nchunks + 5)
+      store_o(nchunks - 1, std::false_type(), c);  // not reached inside the loop
 
     if (write_final && holds_state) {
 #pragma unroll
@@ -673,7 +703,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
             final_state[idx] = sacc[ct][rt][j];
           }
     }
-  } else {
+  } else if (!kHelp || wave < 2 * kChainWaves) {
     // ================================================================ gate wave g: key channels 32g .. 32g+31
     const int g = wave - kChainWaves;
     // -------------------------------------------------------------- gate(x)
@@ -815,26 +845,74 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_bf16_kernel(const bf16* __
     auto step = [&](int i) {
       GateIn gin;
       if (i < nchunks) gate_read(i, gin);
-      if constexpr (!kLoadsOnChain) load_inputs(i, std::false_type());
+      if constexpr (kLoadsOnGate) load_inputs(i, std::false_type());
       if (i < nchunks) {
         if (i < nchunks - 1 || tail == kChunk)
           gate(i, gin, std::false_type());
         else
           gate(i, gin, std::true_type());
       }
-      if constexpr (!kLoadsOnChain) {
+      if constexpr (kLoadsOnGate) {
         wait_inputs();
       }
       block_sync();
     };
 
-    if constexpr (!kLoadsOnChain) {
+    if constexpr (kLoadsOnGate) {
       load_inputs(-2, std::false_type());
       load_inputs(-1, std::false_type());
       wait_inputs();
     }
     block_sync();
     for (int i = 0; i < nsteps; ++i) step(i);
+  } else if constexpr (kHelp) {
+    // ================================================================ helper wave b (two workgroups per sequence)
+    // Everything around the chain waves' serial step that is not the gate:
+    // helper b loads tensor b (and beta), forms W for key channels 32b ..
+    // 32b+31 and takes one more part: 0 the O stores, 1 Gram N, 2 Gram A, 3
+    // the solve.  The chain waves are then left with U and the serial step.
+    const int b = wave - 2 * kChainWaves;
+    auto hiter = [&](int i, auto all, auto role) __attribute__((always_inline)) {
+      constexpr bool kAll = decltype(all)::value;
+      constexpr int kRole = decltype(role)::value;
+      const int r = kRole >= 0 ? kRole : b;
+      // the stores go out before the input loads, which wait_inputs then leaves in flight
+      if (!kStateOnly && r == 0 && (kAll || (i >= 5 && i - 5 < nchunks))) store_o(i - 5, all, 0);
+      load_qka(i, all);
+      if (kAll || (i >= 3 && i - 3 < nchunks)) prep_w(i - 3, r, m_frag(i - 3));
+      load_v(i, all);
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 1) gram(i - 1, std::true_type(), std::false_type());
+      if ((kAll || (i >= 1 && i - 1 < nchunks)) && r == 2 && !kStateOnly)
+        gram(i - 1, std::false_type(), std::true_type());
+      if ((kAll || (i >= 2 && i - 2 < nchunks)) && r == 3) solve(i - 2);
+      wait_inputs();
+      block_sync();
+    };
+    load_inputs(-2, std::false_type());
+    load_inputs(-1, std::false_type());
+    wait_inputs();
+    block_sync();  // inputs of chunk 0 in LDS
+    using RunTimeRole = std::integral_constant<int, -1>;
+    // the same iterations as the chain waves' loop, in one copy per helper
+    int i = 0;
+    for (; i < 6 && i < nsteps; ++i) hiter(i, std::false_type(), RunTimeRole());
+    auto steady = [&](auto role) __attribute__((always_inline)) {
+      for (; i + 1 <= nchunks - 4; i += 2) {
+        hiter(i, std::true_type(), role);
+        hiter(i + 1, std::true_type(), role);
+      }
+    };
+    if (b == 0)
+      steady(std::integral_constant<int, 0>());
+    else if (b == 1)
+      steady(std::integral_constant<int, 1>());
+    else if (b == 2)
+      steady(std::integral_constant<int, 2>());
+    else
+      steady(std::integral_constant<int, 3>());
+    for (; i < nsteps; ++i) hiter(i, std::false_type(), RunTimeRole());
+    if (!kStateOnly && b == 0 && nchunks > 0 && nsteps < nchunks + 5)
+      store_o(nchunks - 1, std::false_type(), 0);  // not reached inside the loop
   }
 }
 
@@ -902,7 +980,8 @@ hipError_t launch_chunk_fwd_bf16(const void* q, const void* k, const void* v, co
   auto launch = [&](int parts, int u0, int u1) {
     const unsigned grid =
         parts == 1 ? (unsigned)(u1 - u0) : (unsigned)(8 * parts * (((int64_t)(u1 - u0) + 7) / 8));
-    hipLaunchKernelGGL(parts == 4 ? k_quarters : parts == 2 ? k_pairs : k_single, dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL(parts == 4 ? k_quarters : parts == 2 ? k_pairs : k_single, dim3(grid),
+                       dim3(threads_of(parts == 4 ? 4 : parts == 2 ? 1 : 2)), 0,
                        stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)a, beta, initial_state,
                        (bf16*)o, final_state, T, H, u0, u1, opt.states, opt.state_every, opt.n_states, opt.cu_seqlens,
                        opt.seg_len, opt.seg_count, opt.last_only ? 1 : 0, norm ? (const bf16*)opt.z : nullptr,
