@@ -616,22 +616,30 @@ def test_varlen_equal_lengths_match_batched(kda, dtype):
     assert torch.equal(o_p, o_b.reshape(N * T, H, 128)) and torch.equal(S_p, S_b)
 
 
+# (sequences, heads): 99 (sequence, head) pairs run as two workgroups each; 291 as a
+# round of single workgroups, then the other 35 as four each; 356 as single
+# workgroups, then the other 100 as two each (on a 256-CU device)
+VARLEN_LAYOUTS = {"two": (33, 3), "one+four": (97, 3), "one+two": (89, 4)}
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_varlen_many_sequences_both_layouts(kda, dtype):
-    """97 sequences x 3 heads = 291 (sequence, head) pairs on a 256-CU
-    device: single workgroups, then pairs; random lengths 0..70 with clamped
-    bogus offsets at the end (N + 1 offsets, the last two past T)."""
+@pytest.mark.parametrize("layout", list(VARLEN_LAYOUTS))
+def test_varlen_many_sequences_each_layout(kda, dtype, layout):
+    """Many packed sequences with random lengths 0..330 (the longer ones
+    reach the steady-state loop) in each launch layout, with clamped bogus
+    offsets at the end (N + 1 offsets, the last two past T); every
+    sequence's final state against the oracle."""
     import torch
 
-    w = variant(WORKLOADS[2], index=153, dtype=dtype)
-    rng = np.random.default_rng(9)
-    lengths = rng.integers(0, 71, size=95).tolist()
-    H = 3
+    N_real, H = VARLEN_LAYOUTS[layout]
+    w = variant(WORKLOADS[2], index=153 + N_real, dtype=dtype)
+    rng = np.random.default_rng(9 + N_real)
+    lengths = rng.integers(0, 331, size=N_real - 2).tolist()
     x, h, cu, _ = _packed(w, lengths, H, dtype)
     T = int(cu[-1])
     cu_all = np.concatenate([cu, [T + 50, T + 9]]).astype(np.int32)  # two more sequences, both empty after clamping
     N = len(cu_all) - 1
-    print_case(f"case varlen many {dtype} N={N} T={T} H={H}")
+    print_case(f"case varlen many {dtype} {layout} N={N} T={T} H={H}")
     o, S = kda.kda_chunk_fwd_varlen(x["q"][0], x["k"][0], x["v"][0], x["a"][0], x["beta"][0],
                                     torch.tensor(cu_all, device="cuda"))
     torch.cuda.synchronize()
