@@ -604,8 +604,8 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
       zbuf = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (4 * c + h) * tok_bytes + 16 * n, 0, 0));
     };
 
-    // With the loads here, beta, q, k and a of chunk x land during
-    // iteration x-2.
+    // With the loads here (four workgroups per sequence), beta, q, k and a
+    // of chunk x land during iteration x-2.
     if constexpr (kLoadsOnChain) {
       load_inputs(-2, std::false_type());
       load_inputs(-1, std::false_type());
@@ -840,8 +840,8 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
       if (gt == 0) sm.r5[x % 5].gamma_c[n >> 2][n & 3][2 * g + (h & 1)] = gam_c;
     };
 
-    // With the loads here, as on the chain waves with two workgroups per
-    // sequence: beta, q, k and a of chunk x land during iteration x-2.
+    // With the loads here (one workgroup per sequence), as wherever they are
+    // issued: beta, q, k and a of chunk x land during iteration x-2.
     auto step = [&](int i) {
       GateIn gin;
       if (i < nchunks) gate_read(i, gin);
