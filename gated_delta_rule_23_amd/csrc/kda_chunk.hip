@@ -111,6 +111,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   // round robin, so all parts of a unit share an XCD and its L2).
   static_assert(kParts == 1 || kParts == 2 || kParts == 4, "one, two or four workgroups per unit");
   constexpr int kChainW = kWaves / kParts;  // waves holding state columns
+  // Four workgroups per unit: the solve and the Gram products rotate over the
+  // waves of SIMDs 2 and 3, the two chain waves having SIMDs 0 and 1 (111
+  // against 116 us on 2 heads x 512 tokens, rotating over all six).
+  constexpr int kOffChain[4] = {2, 3, 6, 7};
   const int unit = kParts > 1 ? 8 * (int)(blockIdx.x / (8 * kParts)) + (int)(blockIdx.x & 7) : (int)blockIdx.x;
   const int part = kParts > 1 ? (int)((blockIdx.x >> 3) % kParts) : 0;
   if (unit >= args.units) return;  // whole workgroup, before any barrier
@@ -144,7 +148,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, h = lane >> 4;
-  const int gch = 16 * wave + n;  // key channel of this lane's gate
+  // The gate: wave w gates key channels 16w .. 16w+15 (group w).  With four
+  // workgroups per unit the two chain waves gate none: waves 6 and 7 (SIMDs
+  // 2 and 3) also gate their groups 0 and 1.
+  constexpr bool kGatePairs = kParts == 4;
+  constexpr int kGS = kGatePairs ? 2 : 1;  // gate groups per wave, at most
+  const bool gate_wave = !kGatePairs || wave >= 2;
+  const int n_groups = kGatePairs && wave >= 6 ? 2 : 1;
+  const int g0 = wave;  // the first group; the second (waves 6 and 7) is wave - 6
   // the state column of this lane: chain waves only (the first 8 / kParts)
   const bool chain_wave = wave < kChainW;
   const int col = (kD / kParts) * part + 16 * (wave % kChainW) + n;
@@ -156,10 +167,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   const float* beta_seq = beta + tok0 * H + hh;
   // Byte offsets of this lane's four tokens (4h .. 4h+3) inside a chunk:
   // its gate channel (q, k, a), its state column (v, o) and beta.
-  int off_row[4], off_col[4], off_beta[4];
+  int off_row[kGS][4], off_col[4], off_beta[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    off_row[j] = (int)(((4 * h + j) * tok_elems + gch) * (int64_t)sizeof(IO));
+#pragma unroll
+    for (int gs = 0; gs < kGS; ++gs)
+      off_row[gs][j] = (int)(((4 * h + j) * tok_elems + 16 * (gs == 0 ? g0 : max(wave - 6, 0)) + n) * (int64_t)sizeof(IO));
     off_col[j] = (int)(((4 * h + j) * tok_elems + col) * (int64_t)sizeof(IO));
     off_beta[j] = (4 * h + j) * H * (int)sizeof(float);
   }
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   // element keeps its own 32-bit register, so no wait follows the loads: they
   // complete under the next iteration's work.
   struct Regs {
-    uint32_t q[4], k[4], a[4], v[4];
+    uint32_t q[kGS][4], k[kGS][4], a[kGS][4], v[4];
     float b[4];
   };
   // x: chunk index; rows_off / beta_off: x chunk strides in bytes
@@ -216,11 +229,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
                  rb = make_rsrc(b_seq + beta_off, beta_bytes(x));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      r.q[j] = Raw<IO>::load(rq, off_row[j]);
-      r.k[j] = Raw<IO>::load(rk, off_row[j]);
-      // the gate logit as fp32 bits (zero-sized resources return 0 without reading)
-      r.a[j] = gate_mode == kGateScalar ? __builtin_amdgcn_raw_buffer_load_b32(rg, off_beta[j], 0, 0)
-                                        : __float_as_uint(Raw<IO>::f32(Raw<IO>::load(ra, off_row[j])));
+#pragma unroll
+      for (int gs = 0; gs < kGS; ++gs) {
+        if (gs >= n_groups) break;
+        r.q[gs][j] = Raw<IO>::load(rq, off_row[gs][j]);
+        r.k[gs][j] = Raw<IO>::load(rk, off_row[gs][j]);
+        // the gate logit as fp32 bits (zero-sized resources return 0 without reading)
+        r.a[gs][j] = gate_mode == kGateScalar
+                         ? __builtin_amdgcn_raw_buffer_load_b32(rg, off_beta[j], 0, 0)
+                         : __float_as_uint(Raw<IO>::f32(Raw<IO>::load(ra, off_row[gs][j])));
+      }
       r.b[j] = load_f32(rb, off_beta[j]);
     }
   };
@@ -242,20 +260,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     return frag4<OT>(d);
   };
 
-  // ------------------------------------------------ gate: this lane's channel, tokens 4h .. 4h+3
-  auto gate = [&](const Regs& cur, Stage<OT>& st, int nvalid, auto ragged) {
+  // ------------------------------------------------ gate: group g (g0, or wave - 6 for gs = 1), lane channel 16 g + l%16, tokens 4h .. 4h+3
+  auto gate = [&](const Regs& cur, int gs, Stage<OT>& st, int nvalid, auto ragged) {
+    const int g = gs == 0 ? g0 : wave - 6, gch = 16 * g + n;
     float b[4];
     float run = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // no gate: g = 0 (alpha = 1)
-      float g2 = gate_mode == kGateNone ? 0.0f : kGateLog2 * sigmoid_fast(__uint_as_float(cur.a[j]));
+      float g2 = gate_mode == kGateNone ? 0.0f : kGateLog2 * sigmoid_fast(__uint_as_float(cur.a[gs][j]));
       if constexpr (decltype(ragged)::value) g2 = 4 * h + j < nvalid ? g2 : 0.0f;  // padded tokens: g = 0
       run += g2;
       b[j] = run;
     }
     // prefix over the four token groups of this channel, through LDS
-    float* pre = &sm.prefix[wave][n][0];
+    float* pre = &sm.prefix[g][n][0];
     pre[h] = run;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // lanes read each other's writes
     __builtin_amdgcn_wave_barrier();
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
       const float b2 = b[j] + prefix;
       const float gam = __builtin_amdgcn_exp2f(b2);
       const float inv = __builtin_amdgcn_exp2f(-b2);
-      const float kk = Raw<IO>::f32(cur.k[j]), qq = Raw<IO>::f32(cur.q[j]);  // zero past T
+      const float kk = Raw<IO>::f32(cur.k[gs][j]), qq = Raw<IO>::f32(cur.q[gs][j]);  // zero past T
       kh[j] = kk * gam;
       qh[j] = qq * gam;
       kt[j] = kk * inv;
@@ -282,13 +301,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     mfma_k16(tkh, frag4<OT>(kh), ident);
     mfma_k16(tqh, frag4<OT>(qh), ident);
     mfma_k16(tkt, frag4<OT>(kt), ident);
-    store_frag4<OT>(&st.kbf[wave][lane][0], frag4<OT>(kbar));  // already channel-major
+    store_frag4<OT>(&st.kbf[g][lane][0], frag4<OT>(kbar));  // already channel-major
     if (h == 0) st.gamma_c[gch] = gam_c;
     if (n == 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st.beta[4 * h + j] = cur.b[j];  // zero past T
     }
-    const int kb_w = wave >> 1, so = 4 * (wave & 1);
+    const int kb_w = g >> 1, so = 4 * (g & 1);
     store_frag4<OT>(&st.xf[0][kb_w][lane][so], frag4<OT>(tkh));
     store_frag4<OT>(&st.xf[1][kb_w][lane][so], frag4<OT>(tqh));
     store_frag4<OT>(&st.kf[kb_w][lane][so], frag4<OT>(tkt));
@@ -298,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   int64_t rows_next = rows_step, beta_next = beta_step;
   auto step = [&](int i, const Regs& cur, Regs& nxt) {
     // ------------------------------------------------ loads for the next iteration
-    load_gate_inputs(i + 1, rows_next, beta_next, nxt);
+    if (gate_wave) load_gate_inputs(i + 1, rows_next, beta_next, nxt);
     if (chain_wave) load_chain_inputs(i - 2, rows_next - 3 * rows_step, nxt);
 
     // ------------------------------------------------ chain(i - 3): the serial part
@@ -358,7 +377,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     // ------------------------------------------------ solve(i - 2): one wave
     // (several workgroups per unit: on the waves that hold no state)
     if (i - 2 >= 0 && i - 2 < nchunks &&
-        wave == (kParts > 1 ? kChainW + (i - 2) % (kWaves - kChainW) : (i - 2) % kWaves)) {
+        wave == (kParts == 4   ? kOffChain[(i - 2) & 3]
+                 : kParts > 1 ? kChainW + (i - 2) % (kWaves - kChainW)
+                              : (i - 2) % kWaves)) {
       Stage<OT>& st = sm.st[(i - 2) % kStages];
       const Frag4<OT> fnt = load_frag4<OT>(&st.nf[0][lane][0]);
       const Frag4<OT> fnc = load_frag4<OT>(&st.nf[1][lane][0]);
@@ -386,7 +407,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
 
     // ------------------------------------------------ gram(i - 1): another wave, another SIMD
     if (i - 1 >= 0 && i - 1 < nchunks &&
-        wave == (kParts > 1 ? kChainW + (i + 1) % (kWaves - kChainW) : (i + 3) % kWaves)) {
+        wave == (kParts == 4   ? kOffChain[(i + 1) & 3]
+                 : kParts > 1 ? kChainW + (i + 1) % (kWaves - kChainW)
+                              : (i + 3) % kWaves)) {
       Stage<OT>& st = sm.st[(i - 1) % kStages];
       // C layouts (lane (n, h), register j <-> row r = 4h + j, column n):
       //   gkt = Kt Kh^T = (Kh Kt^T)^T,  gqt = Kt Qh^T = (Qh Kt^T)^T
@@ -411,13 +434,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
     }
 
     // ------------------------------------------------ gate(i)
-    if (i < nchunks) {
+    if (i < nchunks && gate_wave) {
       const int nvalid = min(kChunk, T - i * kChunk);
       Stage<OT>& st = sm.st[i % kStages];
-      if (nvalid == kChunk)
-        gate(cur, st, nvalid, std::false_type());
-      else
-        gate(cur, st, nvalid, std::true_type());
+#pragma unroll
+      for (int gs = 0; gs < kGS; ++gs) {
+        if (gs >= n_groups) break;
+        if (nvalid == kChunk)
+          gate(cur, gs, st, nvalid, std::false_type());
+        else
+          gate(cur, gs, st, nvalid, std::true_type());
+      }
     }
 
     __syncthreads();
@@ -426,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(const IO* __restric
   };
 
   Regs A, B;
-  load_gate_inputs(0, 0, 0, A);
+  if (gate_wave) load_gate_inputs(0, 0, 0, A);
   for (int i = 0; i < nchunks + 3; i += 2) {
     step(i, A, B);
     step(i + 1, B, A);
