@@ -501,6 +501,15 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
     f32x4 ua[kCT], ub[kCT];
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) ua[ct] = ub[ct] = f32x4{0, 0, 0, 0};
+    // With the helper waves, Gamma_C of the chunk the next iteration's chain
+    // step takes is read one iteration early (two sets alternate like the U
+    // tiles), so that the decay of S runs under that step's first MFMAs
+    // instead of waiting on an LDS read issued after the barrier (398.8 ->
+    // 383.4 us on 8K tokens x 96 heads; no change in the other layouts, which
+    // read it in the step).
+    constexpr bool kGcAhead = kHelp;
+    f32x4 gca[2], gcb[2];
+    gca[0] = gca[1] = gcb[0] = gcb[1] = f32x4{0, 0, 0, 0};
 
     // ------------------------------------------------------------ prep(x): W and U tiles
     // W for key channels 32c .. 32c+31 (on the helper waves when there are
@@ -521,7 +530,7 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
     };
 
     // ------------------------------------------------------------ chain(x): the serial part
-    auto chain = [&](int x, const f32x4 (&u)[kCT]) {
+    auto chain = [&](int x, const f32x4 (&u)[kCT], const f32x4 (&gcv)[2]) {
       const bf16* tw = &sm.r2[x & 1].w[0][0];
       const bf16* tq = &sm.r5[x % 5].qh[0][0];
       const bf16* tb = &sm.r5[x % 5].kb[0][0];
@@ -538,8 +547,15 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) fkb[rt] = f4(lds_b64(tb + 16 * rt * kChunk + pl_sw));  // A layout of Kb^T
       // Gamma_C[16 rt + 4h + l%4] for all rt; row 16 rt + 4h + j comes from lane j of the quad
-      const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.r5[x % 5].gamma_c[h][n & 3][0]);
-      const f32x4 g_lo = gp[0], g_hi = gp[1];
+      f32x4 g_lo, g_hi;
+      if constexpr (kGcAhead) {
+        g_lo = gcv[0];
+        g_hi = gcv[1];
+      } else {
+        const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.r5[x % 5].gamma_c[h][n & 3][0]);
+        g_lo = gp[0];
+        g_hi = gp[1];
+      }
       f32x4 pw[kCT], pq[kCT];
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
@@ -619,19 +635,28 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
     // two waves without state take them: 4 both Gram products, 5 the solve;
     // with two, the helper waves do, and the chain waves take none.  kRole <
     // 0 looks it up at run time.
-    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], auto all, auto role)
+    auto citer = [&](int i, const f32x4 (&u_use)[kCT], f32x4 (&u_make)[kCT], const f32x4 (&g_use)[2],
+                     f32x4 (&g_make)[2], auto all, auto role)
                      __attribute__((always_inline)) {
       constexpr bool kAll = decltype(all)::value;
       constexpr int kRole = decltype(role)::value;
       constexpr int kRoleOf[kChainWaves] = {3, kParts == 4 ? 3 : 0, kParts == 4 ? 4 : 1, kParts == 4 ? 5 : 2};
       const int r = kHelp ? 3 : kRole >= 0 ? kRole : kRoleOf[c];
+      // Gamma_C of chunk i - 3 for the next iteration's chain step (gate(i - 3)
+      // wrote it; its ring slot is next written by gate(i + 2))
+      if constexpr (kGcAhead && kGate != kGateNone)
+        if (holds_state && (kAll || (i >= 3 && i - 3 < nchunks))) {
+          const f32x4* gp = reinterpret_cast<const f32x4*>(&sm.r5[(i - 3) % 5].gamma_c[h][n & 3][0]);
+          g_make[0] = gp[0];
+          g_make[1] = gp[1];
+        }
       // the stores go out before the input loads, which wait_inputs then leaves in flight
       if (!kHelp && !kStateOnly && stores_o(c) && (kAll || (i >= 5 && i - 5 < nchunks))) store_o(i - 5, all, c);
       if (kNorm && (kAll || (i >= 4 && i - 4 < nchunks))) load_z(i - 4, all);
       if constexpr (kLoadsOnChain) load_qka(i, all);
       if (kAll || (i >= 3 && i - 3 < nchunks)) prep(i - 3, u_make);
       if constexpr (kLoadsOnChain) load_v(i, all);
-      if (holds_state && (kAll || (i >= 4 && i - 4 < nchunks))) chain(i - 4, u_use);
+      if (holds_state && (kAll || (i >= 4 && i - 4 < nchunks))) chain(i - 4, u_use, g_use);
       if constexpr (kEmit)
         if (holds_state && i - 3 == next_emit && next_emit <= last_emit) {  // chunk i - 4 ends a checkpoint interval
           emit_state(i - 4);
@@ -655,8 +680,8 @@ __global__ __launch_bounds__(threads_of(kLay)) void chunk_fwd_bf16_kernel(const 
       block_sync();
     };
     auto step2 = [&](int i, auto all, auto role) __attribute__((always_inline)) {
-      citer(i, ua, ub, all, role);
-      citer(i + 1, ub, ua, all, role);
+      citer(i, ua, ub, gca, gcb, all, role);
+      citer(i + 1, ub, ua, gcb, gca, all, role);
     };
     using RunTimeRole = std::integral_constant<int, -1>;
     // Iterations 5 <= i <= nchunks - 4 have every section active and load a
