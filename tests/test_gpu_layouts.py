@@ -140,3 +140,32 @@ def test_layouts_agree_bit_for_bit(kda, dtype):
         hh = o.shape[2]
         assert torch.equal(o, full_o[:, :, :hh]), name
         assert torch.equal(S, full_S[:, :hh]), name
+
+
+# Lengths around the two-workgroup loop's boundaries: one partial chunk, one
+# whole chunk, 3, 4 and 6 chunks (only the iterations with range tests, in
+# which the chain waves also read each chunk's Gamma_C one iteration ahead),
+# 11 chunks (the shortest with iterations without range tests), 12, and 14
+# with a ragged last chunk.
+PAIR_T = [1, 16, 33, 64, 96, 176, 192, 217]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_two_workgroup_layout_short_lengths(kda, dtype):
+    """100 units (two workgroups each) at each length of PAIR_T, with S0, against the oracle per sequence."""
+    import torch
+
+    B, H = SHAPES["two"]
+    for T_ in PAIR_T:
+        w = variant(WORKLOADS[2], index=520 + T_, dtype=dtype, s0_scale=0.5)
+        print_case(f"case two-workgroup layout {dtype} B={B} H={H} T={T_}")
+        x = device_inputs(w, B=B, T=T_, H=H)
+        o, S = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], initial_state=x["s0"])
+        torch.cuda.synchronize()
+        h = host_inputs(w, nb=B, nt=T_, nh=H)
+        o_ref, S_ref = oracle.forward(synth.to_f64(h["q"]), synth.to_f64(h["k"]), synth.to_f64(h["v"]),
+                                      h["beta"].astype(np.float64), a=synth.to_f64(h["a"]),
+                                      s0=h["s0"].astype(np.float64))
+        wo, ws = worst(to_np(o), o_ref, (1, 3)), worst(to_np(S), S_ref, (2, 3))
+        print_case(f"  worst per sequence: o {wo:.3e}, S {ws:.3e}")
+        assert wo <= TOL[dtype] and ws <= TOL[dtype], T_
